@@ -1,0 +1,145 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * What the library computes.  For every batch b, head h and query row i:
+ *
+ *     s_ij = scale * sum_c q[b,h,i,c] * k[b,h,j,c]     for the visible keys j
+ *     o[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,h,j,:]
+ *     lse[b,h,i] = log sum_j exp(s_ij)                (natural log)
+ *
+ * This is the attention of Golden et al., "Is Flash Attention Stable?",
+ * sec. II-A (softmax(Q K^T / sqrt(d_k)) V; the caller passes the factor as
+ * `scale`), evaluated the FlashAttention way described in the same paper's
+ * sec. II-B and in the yadro-code tutorial "How FlashAttention reduces GPU
+ * memory traffic": key tiles are folded into a running row maximum, a running
+ * sum of exponentials and an unnormalised output that is rescaled by
+ * exp(m_old - m_new) whenever the maximum grows, and divided by the sum once at
+ * the end.  The N x N score matrix is never stored.
+ *
+ * Visibility: key j is visible to query i unless `causal` is set and j > i
+ * (the causal prefix of the tutorial's self-check), or key_padding_mask[b*N+j]
+ * is non-zero.  Masked scores are a true -infinity, never a finite stand-in
+ * (the first page warns about a hard-coded -50,000 in one library's kernels).
+ * A row with no visible key has no softmax; this library defines its output as
+ * +0.0 in every element and lse = -infinity.
+ *
+ * Conventions shared by every entry point below:
+ *   - q, k, v, o: DEVICE pointers, contiguous [B][H][N][d] row-major, element
+ *     type given by `dtype` (see attn_dtype), 16-byte aligned.  The caller owns
+ *     them.  o must not overlap q, k, v or lse.
+ *   - lse: DEVICE pointer to [B][H][N] float, 4-byte aligned, or NULL (then no
+ *     lse is written).
+ *   - key_padding_mask: DEVICE pointer to [B][N] bytes (non-zero = padded key,
+ *     excluded from every query row of that batch), or NULL (no padding).
+ *   - B, H, N >= 0 (any zero is a successful no-op), B*H*N < 2^31,
+ *     d in {64, 128}; scale finite and > 0 (1/sqrt(d) in the usual use).
+ *   - stream: a hipStream_t passed as void*; NULL is the null stream.  Every
+ *     call is asynchronous on that stream; outputs are valid once the caller
+ *     has synchronised it.  No entry point synchronises, allocates device
+ *     memory, or keeps state beyond a thread-local error string.
+ *   - Errors: arguments are checked on the host before anything is launched; a
+ *     failed check returns its status and writes nothing.  A launch failure
+ *     returns ATTN_ERR_HIP.  attn_last_error() then holds a message.  No
+ *     exception and no abort crosses this interface.
+ *   - Determinism: identical inputs and options give bitwise-identical o and
+ *     lse (no atomics, fixed reduction order).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o.  In the *_OUT_F32 flavours q, k, v are 16-bit
+ * and o is written as float; the kernel and its arithmetic are the same, only
+ * the final store differs. */
+enum attn_dtype {
+    ATTN_F32 = 0,          /* q, k, v, o float; fp32 matrix-core products, fp32 P      */
+    ATTN_F16 = 1,          /* q, k, v, o IEEE half; P rounded to half for P.V           */
+    ATTN_BF16 = 2,         /* q, k, v, o bfloat16; P rounded to bfloat16 for P.V        */
+    ATTN_F16_OUT_F32 = 3,  /* q, k, v half; o float                                      */
+    ATTN_BF16_OUT_F32 = 4  /* q, k, v bfloat16; o float                                  */
+};
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* a required pointer is NULL                               */
+    ATTN_ERR_SHAPE = 2,     /* negative size, or B*H*N too large                        */
+    ATTN_ERR_HEAD_DIM = 3,  /* d not in {64, 128}                                       */
+    ATTN_ERR_DTYPE = 4,     /* unknown dtype                                            */
+    ATTN_ERR_ALIGN = 5,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned   */
+    ATTN_ERR_TILE = 6,      /* tile shape or kv_order not supported                     */
+    ATTN_ERR_SCALE = 7,     /* scale not finite or not > 0                              */
+    ATTN_ERR_ALIAS = 8,     /* o overlaps an input or lse                               */
+    ATTN_ERR_HIP = 9,       /* the HIP runtime reported an error                        */
+    ATTN_ERR_WORKSPACE = 10 /* naive baseline: workspace NULL or too small              */
+};
+
+/* Tile and fold-order options (attn_fwd_ex).
+ *   br: query rows per workgroup tile, one of 16, 32, 64, 128 (0 = default).
+ *   bc: keys per key tile, one of 16, 32, 64, 128 (0 = default).  bc is also the
+ *       rescaling granularity: the running maximum is updated once per tile.
+ *   kv_order: 0 folds each row's key tiles first to last, 1 last to first.
+ * The tile sizes and block order are the knobs the stability paper's
+ * sequence-length and perturbation sweeps vary (its Figs. 5 and 6). */
+typedef struct attn_opts {
+    int br;
+    int bc;
+    int kv_order;
+    int reserved[5];   /* must be zero */
+} attn_opts;
+
+/* Exact attention forward with the default tiles and ascending fold order. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* key_padding_mask, int dtype, void* stream);
+
+/* Same as attn_fwd with explicit tiles and fold order; opts NULL = defaults. */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* key_padding_mask, int dtype, void* stream,
+                const attn_opts* opts);
+
+/* Host-only argument check of attn_fwd_ex: returns the status attn_fwd_ex would
+ * return before launching anything.  Touches no device and no pointer. */
+int attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, int dtype, const attn_opts* opts);
+
+/* Default (br, bc) that attn_fwd uses for this dtype, head size and causality.
+ * Returns ATTN_OK, or ATTN_ERR_DTYPE / ATTN_ERR_HEAD_DIM. */
+int attn_default_tiles(int dtype, int d, int causal, int* br, int* bc);
+
+/* Baseline attention that materialises the score matrix, for comparison only
+ * (the stability paper's "baseline attention").  S = scale*q k^T is stored in
+ * the workspace in the input type (float for ATTN_F32), the row softmax P is
+ * computed in fp32 and stored back in the input type, then o = P v with fp32
+ * accumulation.  Masking, fully masked rows and lse follow attn_fwd.
+ * workspace: DEVICE pointer of at least attn_naive_workspace_bytes() bytes,
+ * 16-byte aligned, owned by the caller. */
+int attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* key_padding_mask, int dtype, void* stream,
+                   void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes attn_naive_fwd needs: B*H*N*N elements of the input type. */
+size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/* Static description of a status code. */
+const char* attn_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,90 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+(Addresses below are fake integers; a rejected call never dereferences them.)"""
+import os
+import re
+
+import pytest
+
+import tiled_online_softmax_fwd_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, HEAD, DTYPE, ALIGN, TILE, SCALE, ALIAS = 0, 1, 2, 3, 4, 5, 6, 7, 8
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", src, flags=re.M))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert names == set(A.EXPORTS), names ^ set(A.EXPORTS)
+    lib = A.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert A.version() == 100
+    assert A.lib().attn_status_string(0) == b"ok"
+    assert A.lib().attn_status_string(9) == b"HIP runtime error"
+    assert A.lib().attn_status_string(123) == b"unknown status"
+
+
+def test_default_tiles():
+    assert A.default_tiles(A.BF16, 128, True) == (128, 64)
+    with pytest.raises(A.AttnError):
+        A.default_tiles(A.BF16, 96)
+    with pytest.raises(A.AttnError):
+        A.default_tiles(9, 64)
+
+
+BASE = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x50000)
+
+
+def chk(B=1, H=2, N=8, d=64, scale=0.125, causal=0, dtype=A.BF16, br=0, bc=0, kv_order=0, **ptrs):
+    p = dict(BASE)
+    p.update(ptrs)
+    return A.check_args(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, N, d, scale, causal, None, dtype,
+                        br, bc, kv_order)
+
+
+def test_valid_arguments_pass():
+    assert chk() == OK
+    assert chk(dtype=A.F32) == OK and chk(dtype=A.F16_OUT_F32) == OK and chk(d=128) == OK
+    assert chk(lse=None) == OK
+    for br in (32, 64, 128):
+        for bc in (32, 64, 128):
+            for order in (0, 1):
+                assert chk(br=br, bc=bc, kv_order=order) == OK
+
+
+def test_rejections():
+    assert chk(q=None) == NULL and chk(o=None) == NULL
+    assert chk(B=-1) == SHAPE and chk(N=-5) == SHAPE
+    assert chk(B=1 << 16, H=1 << 10, N=1 << 6) == SHAPE
+    assert chk(d=96) == HEAD and chk(d=0) == HEAD
+    assert chk(dtype=5) == DTYPE and chk(dtype=-1) == DTYPE
+    assert chk(q=0x10008) == ALIGN and chk(lse=0x50002) == ALIGN
+    assert chk(br=48) == TILE and chk(bc=256) == TILE and chk(kv_order=2) == TILE
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert chk(scale=bad) == SCALE
+    assert chk(o=0x10000 + 16) == ALIAS                     # o inside q
+    assert chk(lse=0x40000 + 64) == ALIAS                   # lse inside o
+    assert A.lib().attn_last_error() != b""
+
+
+def test_zero_sizes_need_no_pointers():
+    assert chk(B=0, q=None, k=None, v=None, o=None) == OK
+    assert chk(N=0, q=None, k=None, v=None, o=None) == OK
+    assert chk(N=0, d=96) == HEAD         # shape rules still apply
+
+
+def test_no_cpu_fallback_exists():
+    """The binding has no code path that computes attention itself."""
+    src = open(os.path.join(ROOT, "tiled_online_softmax_fwd_amd", "__init__.py")).read()
+    for banned in (r"softmax\(", r"matmul", r"\boracle\b", r"einsum", r"import numpy", r"\bexp\(", r"\bbmm\("):
+        assert not re.search(banned, src), banned

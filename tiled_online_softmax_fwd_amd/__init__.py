@@ -1,0 +1,169 @@
+"""Python binding of libattn.so, the gfx950 exact-attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/attn.h.  PyTorch is used for device memory
+and streams; tensors are passed by data_ptr() on torch's current HIP stream.
+There is no fallback: if the library is missing or the GPU is absent, calls
+raise.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+# attn_dtype
+F32, F16, BF16, F16_OUT_F32, BF16_OUT_F32 = 0, 1, 2, 3, 4
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEAD_DIM",
+          4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_TILE", 7: "ATTN_ERR_SCALE",
+          8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
+           "attn_naive_workspace_bytes", "attn_status_string", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class attn_opts(ctypes.Structure):
+    _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int), ("kv_order", ctypes.c_int),
+                ("reserved", ctypes.c_int * 5)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not built; run __graft_entry__.build() or "
+                               "python tiled_online_softmax_fwd_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        common = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
+        L.attn_fwd.argtypes = common + [vp]
+        L.attn_fwd_ex.argtypes = common + [vp, ctypes.POINTER(attn_opts)]
+        L.attn_check_args.argtypes = common + [ctypes.POINTER(attn_opts)]
+        L.attn_default_tiles.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        L.attn_naive_fwd.argtypes = common + [vp, vp, ctypes.c_size_t]
+        L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
+        L.attn_naive_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_status_string.argtypes = [i]
+        L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_version.argtypes = []
+        for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_check_args, L.attn_default_tiles,
+                   L.attn_naive_fwd, L.attn_version):
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _raise(st):
+    if st != 0:
+        raise AttnError(st, lib().attn_last_error().decode())
+
+
+def make_opts(br=0, bc=0, kv_order=0):
+    o = attn_opts()
+    o.br, o.bc, o.kv_order = int(br or 0), int(bc or 0), int(kv_order or 0)
+    return o
+
+
+def default_tiles(dtype, d, causal=False):
+    br, bc = ctypes.c_int(), ctypes.c_int()
+    _raise(lib().attn_default_tiles(int(dtype), int(d), int(bool(causal)), ctypes.byref(br), ctypes.byref(bc)))
+    return br.value, bc.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, out_f32):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16_OUT_F32 if out_f32 else F16
+    if t.dtype == torch.bfloat16:
+        return BF16_OUT_F32 if out_f32 else BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prep(q, k, v, key_padding_mask, out, lse, out_f32, want_lse):
+    torch = _torch()
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous GPU tensors")
+    B, H, N, d = q.shape
+    code = _dtype_code(q, out_f32)
+    odt = torch.float32 if (out_f32 or q.dtype == torch.float32) else q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if key_padding_mask is not None:
+        if key_padding_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_padding_mask.shape) != (B, N):
+            raise ValueError("key_padding_mask must be a [B, N] uint8/bool tensor")
+        key_padding_mask = key_padding_mask.contiguous()
+    return B, H, N, d, code, out, lse, key_padding_mask
+
+
+def fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=None, lse=None,
+        out_fp32=False, br=None, bc=None, kv_order=0, want_lse=True, stream=None):
+    """Exact attention forward through attn_fwd_ex.  Returns (out, lse)."""
+    torch = _torch()
+    B, H, N, d, code, out, lse, mask = _prep(q, k, v, key_padding_mask, out, lse, out_fp32, want_lse)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    opts = make_opts(br, bc, kv_order)
+    st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                           int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s), ctypes.byref(opts))
+    _raise(st)
+    return out, lse
+
+
+def naive_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=None, lse=None,
+              out_fp32=False, workspace=None, want_lse=True, stream=None):
+    """Materialising baseline through attn_naive_fwd.  Returns (out, lse)."""
+    torch = _torch()
+    B, H, N, d, code, out, lse, mask = _prep(q, k, v, key_padding_mask, out, lse, out_fp32, want_lse)
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    need = lib().attn_naive_workspace_bytes(B, H, N, code)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                              int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s),
+                              _ptr(workspace), workspace.numel())
+    _raise(st)
+    return out, lse
+
+
+def check_args(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale, causal, mask_ptr, dtype,
+               br=0, bc=0, kv_order=0):
+    """Host-only argument check with raw integer addresses; returns the status."""
+    opts = make_opts(br, bc, kv_order)
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib().attn_check_args(c(q_ptr), c(k_ptr), c(v_ptr), c(o_ptr), c(lse_ptr), B, H, N, d,
+                                 float(scale), int(causal), c(mask_ptr), int(dtype), ctypes.byref(opts))
+
+
+def version():
+    return lib().attn_version()

@@ -1,0 +1,245 @@
+// attn_api.cpp -- host side of the C ABI declared in include/attn.h:
+// argument checks (host only, before any HIP call), tile selection, dispatch
+// to the kernel instance tables, and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "fwd_kernel.h"
+#include "naive_kernel.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return ATTN_OK;
+}
+
+size_t elem_bytes_in(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+size_t elem_bytes_out(int dtype) { return (dtype == ATTN_F32 || dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool valid_tile(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
+
+// Defaults per (input type, head size): 128 query rows per workgroup (four
+// waves of 32 rows), 64 keys per tile.
+void defaults(int dtype, int d, int causal, int* br, int* bc)
+{
+    (void)dtype; (void)d; (void)causal;
+    *br = 128;
+    *bc = 64;
+}
+
+attnk::LaunchFn find(int dtype, int d, int br, int bc)
+{
+    switch (dtype) {
+    case ATTN_F32: return attnk::lookup_f32(d, br, bc);
+    case ATTN_F16: case ATTN_F16_OUT_F32: return attnk::lookup_f16(d, br, bc);
+    case ATTN_BF16: case ATTN_BF16_OUT_F32: return attnk::lookup_bf16(d, br, bc);
+    default: return nullptr;
+    }
+}
+
+// Everything that does not involve a pointer.
+int check_scalars(int B, int H, int N, int d, float scale, int dtype)
+{
+    if (dtype < ATTN_F32 || dtype > ATTN_BF16_OUT_F32) return fail(ATTN_ERR_DTYPE, "dtype %d is not an attn_dtype", dtype);
+    if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_SHAPE, "negative size B=%d H=%d N=%d", B, H, N);
+    if ((int64_t)B * H * N >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_SHAPE, "B*H*N = %lld rows exceeds 2^31 - 1", (long long)B * H * N);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_HEAD_DIM, "head size d=%d, supported: 64, 128", d);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_SCALE, "scale %g must be finite and > 0", (double)scale);
+    return ATTN_OK;
+}
+
+int check_pointers(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int dtype)
+{
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+    const void* p16[4] = {q, k, v, o};
+    const char* names[4] = {"q", "k", "v", "o"};
+    for (int i = 0; i < 4; ++i)
+        if ((uintptr_t)p16[i] % 16) return fail(ATTN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    if (lse && ((uintptr_t)lse % 4)) return fail(ATTN_ERR_ALIGN, "lse is not 4-byte aligned");
+    const size_t rows = (size_t)B * H * N;
+    const size_t nin = rows * d * elem_bytes_in(dtype), nout = rows * d * elem_bytes_out(dtype);
+    const size_t nlse = lse ? rows * sizeof(float) : 0;
+    if (overlaps(o, nout, q, nin) || overlaps(o, nout, k, nin) || overlaps(o, nout, v, nin) ||
+        overlaps(o, nout, lse, nlse))
+        return fail(ATTN_ERR_ALIAS, "o overlaps q, k, v or lse");
+    if (overlaps(lse, nlse, q, nin) || overlaps(lse, nlse, k, nin) || overlaps(lse, nlse, v, nin))
+        return fail(ATTN_ERR_ALIAS, "lse overlaps q, k or v");
+    return ATTN_OK;
+}
+
+int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, int* bc, int* order)
+{
+    defaults(dtype, d, causal, br, bc);
+    *order = 0;
+    if (!opts) return ATTN_OK;
+    for (int i = 0; i < 5; ++i)
+        if (opts->reserved[i] != 0) return fail(ATTN_ERR_TILE, "attn_opts.reserved[%d] must be 0", i);
+    if (opts->br != 0) {
+        if (!valid_tile(opts->br)) return fail(ATTN_ERR_TILE, "br=%d not in {16,32,64,128}", opts->br);
+        *br = opts->br;
+    }
+    if (opts->bc != 0) {
+        if (!valid_tile(opts->bc)) return fail(ATTN_ERR_TILE, "bc=%d not in {16,32,64,128}", opts->bc);
+        *bc = opts->bc;
+    }
+    if (opts->kv_order != 0 && opts->kv_order != 1) return fail(ATTN_ERR_TILE, "kv_order=%d not 0 or 1", opts->kv_order);
+    *order = opts->kv_order;
+    return ATTN_OK;
+}
+
+int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              const attn_opts* opts, int* br, int* bc, int* order)
+{
+    int st = check_scalars(B, H, N, d, scale, dtype);
+    if (st) return st;
+    st = resolve_opts(dtype, d, causal, opts, br, bc, order);
+    if (st) return st;
+    if (!find(dtype, d, *br, *bc))
+        return fail(ATTN_ERR_TILE, "no kernel for dtype %d, d=%d, br=%d, bc=%d", dtype, d, *br, *bc);
+    if ((int64_t)B * H * N == 0) return ATTN_OK;
+    return check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_check_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, int dtype, const attn_opts* opts)
+{
+    (void)key_padding_mask;
+    int br, bc, order;
+    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order);
+    return st ? st : ok();
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* key_padding_mask, int dtype, void* stream,
+                const attn_opts* opts)
+{
+    int br, bc, order;
+    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order);
+    if (st) return st;
+    if ((int64_t)B * H * N == 0) return ok();
+
+    attnk::FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask;
+    p.B = B; p.H = H; p.N = N;
+    p.n_qt = (N + br - 1) / br;
+    p.scale = scale;
+    p.c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e), rounded once
+    p.causal = causal ? 1 : 0;
+    p.kv_order = order;
+    p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
+    const hipError_t e = find(dtype, d, br, bc)(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* key_padding_mask, int dtype, void* stream)
+{
+    return attn_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, key_padding_mask, dtype, stream, nullptr);
+}
+
+int attn_default_tiles(int dtype, int d, int causal, int* br, int* bc)
+{
+    if (dtype < ATTN_F32 || dtype > ATTN_BF16_OUT_F32) return fail(ATTN_ERR_DTYPE, "dtype %d is not an attn_dtype", dtype);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_HEAD_DIM, "head size d=%d, supported: 64, 128", d);
+    if (!br || !bc) return fail(ATTN_ERR_NULL, "br and bc must be non-NULL");
+    defaults(dtype, d, causal, br, bc);
+    return ok();
+}
+
+size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype)
+{
+    if (B <= 0 || H <= 0 || N <= 0 || dtype < ATTN_F32 || dtype > ATTN_BF16_OUT_F32) return 0;
+    return (size_t)B * H * (size_t)N * (size_t)N * elem_bytes_in(dtype);
+}
+
+int attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* key_padding_mask, int dtype, void* stream,
+                   void* workspace, size_t workspace_bytes)
+{
+    int st = check_scalars(B, H, N, d, scale, dtype);
+    if (st) return st;
+    if ((int64_t)B * H * N == 0) return ok();
+    st = check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
+    if (st) return st;
+    const size_t need = attn_naive_workspace_bytes(B, H, N, dtype);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16))
+        return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned", need);
+    const size_t nws = need;
+    const size_t rows = (size_t)B * H * N;
+    if (overlaps(workspace, nws, q, rows * d * elem_bytes_in(dtype)) || overlaps(workspace, nws, k, rows * d * elem_bytes_in(dtype)) ||
+        overlaps(workspace, nws, v, rows * d * elem_bytes_in(dtype)) || overlaps(workspace, nws, o, rows * d * elem_bytes_out(dtype)) ||
+        overlaps(workspace, nws, lse, lse ? rows * 4 : 0))
+        return fail(ATTN_ERR_ALIAS, "workspace overlaps an input or output");
+    attnk::NaiveParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask; p.ws = workspace;
+    p.B = B; p.H = H; p.N = N; p.d = d;
+    p.scale = scale;
+    p.causal = causal ? 1 : 0;
+    p.in_kind = dtype == ATTN_F32 ? 0 : ((dtype == ATTN_F16 || dtype == ATTN_F16_OUT_F32) ? 1 : 2);
+    p.out_f32 = elem_bytes_out(dtype) == 4 ? 1 : 0;
+    const hipError_t e = attnk::naive_launch(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "naive launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char* attn_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_SHAPE: return "bad shape";
+    case ATTN_ERR_HEAD_DIM: return "unsupported head size";
+    case ATTN_ERR_DTYPE: return "unknown dtype";
+    case ATTN_ERR_ALIGN: return "misaligned pointer";
+    case ATTN_ERR_TILE: return "unsupported tile or order";
+    case ATTN_ERR_SCALE: return "bad scale";
+    case ATTN_ERR_ALIAS: return "output overlaps an input";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+    }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,496 @@
+// fwd_kernel.h -- gfx950 kernels of the tiled online-softmax attention forward.
+//
+// One workgroup owns BR query rows of one (batch, head) and walks that head's
+// key tiles of BC rows.  Per key tile it (a) stages K and V in LDS, (b) forms
+// the score tile on the matrix cores, (c) updates each query row's running
+// maximum m, running sum of exponentials l and unnormalised output acc -- the
+// online merge of the yadro-code tutorial "How FlashAttention reduces GPU
+// memory traffic" (a bigger maximum rescales l and acc by exp(m_old - m_new))
+// -- and (d) accumulates P.V on the matrix cores.  acc / l is formed once, at
+// the end.  The score tile lives only in registers: the N x N matrix of Golden
+// et al., "Is Flash Attention Stable?", sec. II-B, is never written anywhere.
+//
+// Orientation.  Each wave owns 32 query rows and computes the TRANSPOSED score
+// tile S^T = K Q^T with v_mfma_f32_32x32x16_{bf16,f16} (or 32x32x2_f32): in the
+// 32x32 accumulator lane L holds query column L%32 and 16 key rows
+// {8*(j/4) + 4*(L/32) + j%4}.  A query row's maximum and sum are therefore
+// in-lane reductions plus one v_permlane32_swap, and m, l and the rescale
+// factor are per-lane scalars.  The same registers, converted to the input
+// type, are directly the B operand of O^T += V^T P^T (contraction over keys
+// with a fixed permutation of the key index that V^T's operand reproduces).
+// V^T's operand is read from row-major V in LDS with ds_read_b64_tr_b16.
+//
+// Scores are kept raw (q.k) in fp32; the softmax uses base 2 with the factor
+// c = scale * log2(e) folded into one FMA: p = exp2(s*c - m*c).  Masked scores
+// are -inf.  A row whose maximum is still -inf uses 0 as its reference so that
+// no exp2(-inf - -inf) is ever formed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnk {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const uint8_t* mask;   // [B][N] or nullptr
+    int B, H, N;
+    int n_qt;              // query tiles per (b, h)
+    float scale;           // natural-log domain factor of q.k
+    float c;               // scale * log2(e)
+    int causal;
+    int kv_order;          // 0 ascending key tiles, 1 descending
+    int out_f32;           // o is float instead of the input type
+};
+
+typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xhalf_max(float x)
+{
+    // max over lanes L and L^32: permlane32_swap returns (lower, upper) halves
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, x), false, false);
+    // both halves add (lower + upper) in the same order
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// 16-bit element traits
+template <typename T> struct H16;
+template <> struct H16<__bf16> {
+    using v8 = bf16x8;
+    static __device__ __forceinline__ f32x16 mma32(v8 a, v8 b, f32x16 c)
+    { return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0); }
+};
+template <> struct H16<_Float16> {
+    using v8 = f16x8;
+    static __device__ __forceinline__ f32x16 mma32(v8 a, v8 b, f32x16 c)
+    { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+
+// LDS swizzles, in 16-byte chunks.  CPR = chunks per row.
+// K rows are read 16 bytes per lane with 32 consecutive rows at one column:
+// XOR the chunk with the row so that 16 consecutive rows hit 16 distinct
+// 16-byte bank groups.
+template <int CPR> __device__ __forceinline__ int swz_k(int r, int c)
+{
+    if constexpr (CPR >= 16) return c ^ (r & 15);
+    else return c ^ ((r >> 1) & 7);      // CPR == 8: two rows per 256 bytes
+}
+// 16-bit V rows are read by ds_read_b64_tr_b16: a half wave covers 4 rows x 64
+// bytes; put the 4 rows in 4 distinct 64-byte bank groups.
+template <int CPR> __device__ __forceinline__ int swz_v16(int r, int c)
+{
+    if constexpr (CPR >= 16) return c ^ ((r & 3) << 2);
+    else return c ^ (((r >> 1) & 1) << 2);
+}
+// fp32 V rows are read 4 bytes per lane, 32 lanes on one row and 32 on row+4.
+__device__ __forceinline__ int swz_v32(int r, int c) { return c ^ (((r >> 2) & 1) << 3); }
+
+// Cooperative copy of ROWS x CPR 16-byte chunks from global rows (row stride
+// CPR chunks) into LDS at chunk index r*CPR + SWZ(r, c).  Rows >= rows_valid are
+// zero-filled, so padding keys of a ragged last tile carry V = 0 and never
+// meet a stale or non-finite value.
+template <int ROWS, int CPR, int NT, int KIND>
+__device__ __forceinline__ void stage_tile(u32x4* __restrict__ lds, const u32x4* __restrict__ g,
+                                           int rows_valid, int tid)
+{
+    constexpr int TOTAL = ROWS * CPR;
+    constexpr int ITERS = (TOTAL + NT - 1) / NT;
+    constexpr int BATCH = ITERS < 8 ? ITERS : 8;     // loads in flight per thread
+#pragma unroll
+    for (int it0 = 0; it0 < ITERS; it0 += BATCH) {
+        u32x4 buf[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int idx = tid + (it0 + u) * NT;
+            buf[u] = (u32x4){0u, 0u, 0u, 0u};
+            if (it0 + u < ITERS && (TOTAL % NT == 0 || idx < TOTAL) && idx / CPR < rows_valid) buf[u] = g[idx];
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int idx = tid + (it0 + u) * NT;
+            if (it0 + u < ITERS && (TOTAL % NT == 0 || idx < TOTAL)) {
+                const int r = idx / CPR, c = idx % CPR;
+                int sc;
+                if constexpr (KIND == 0) sc = swz_k<CPR>(r, c);
+                else if constexpr (KIND == 1) sc = swz_v16<CPR>(r, c);
+                else sc = swz_v32(r, c);
+                lds[r * CPR + sc] = buf[u];
+            }
+        }
+    }
+}
+
+// Workgroup -> (b*H + h, query tile).  Causal: heaviest (last) query tiles of
+// every head are issued first.  Consecutive workgroup ids go to consecutive
+// heads, so with a multiple of 8 heads one head's tiles share one XCD's L2
+// (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ void tile_of_block(const FwdParams& p, int& bh, int& qt)
+{
+    const int BH = p.B * p.H;
+    const int lin = blockIdx.x;
+    bh = lin % BH;
+    qt = lin / BH;
+    if (p.causal) qt = p.n_qt - 1 - qt;
+}
+
+// ============================================================ 16-bit, 32x32
+template <typename T, int D, int BR, int BC>
+__global__ void __launch_bounds__(BR * 2)
+fwd_m32_h16(FwdParams p)
+{
+    using TR = H16<T>;
+    using v8 = typename TR::v8;
+    constexpr int NW = BR / 32, NT = NW * 64;
+    constexpr int CPR = D * 2 / 16;            // 16-byte chunks per row
+    constexpr int NKB = BC / 32, DK = D / 16, DB = D / 32, KS = BC / 16;
+    static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
+
+    __shared__ u32x4 sk[BC * CPR];
+    __shared__ u32x4 sv[BC * CPR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    int bh, qt;
+    tile_of_block(p, bh, qt);
+    const int N = p.N;
+    const int b = bh / p.H;
+    const int q0 = qt * BR;
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const T* __restrict__ Q = (const T*)p.q + head;
+    const T* __restrict__ K = (const T*)p.k + head;
+    const T* __restrict__ V = (const T*)p.v + head;
+    const int qi = q0 + wave * 32 + col;       // this lane's query row
+
+    // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7]
+    v8 qf[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+        u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+        if (qi < N) w = *(const u32x4*)(Q + (size_t)qi * D + ks * 16 + hh * 8);
+        qf[ks] = __builtin_bit_cast(v8, w);
+    }
+
+    float m = -INFINITY;       // running raw maximum of q.k over visible keys
+    float l = 0.f;             // this lane's share of the running sum
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+    const int nkt = (N + BC - 1) / BC;
+    int kt_end = nkt;
+    if (p.causal) {
+        const int last_q = min(q0 + BR, N) - 1;
+        kt_end = min(nkt, last_q / BC + 1);
+    }
+    const int wave_q0 = q0 + wave * 32;
+    const float c = p.c;
+
+    for (int it = 0; it < kt_end; ++it) {
+        const int kt = p.kv_order ? (kt_end - 1 - it) : it;
+        const int k0 = kt * BC;
+        const int rows_valid = min(BC, N - k0);
+        __syncthreads();
+        stage_tile<BC, CPR, NT, 0>(sk, (const u32x4*)(K + (size_t)k0 * D), rows_valid, tid);
+        stage_tile<BC, CPR, NT, 1>(sv, (const u32x4*)(V + (size_t)k0 * D), rows_valid, tid);
+        __syncthreads();
+
+        // S^T = K Q^T : 32 keys x 32 queries per block
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = (f32x16){};
+            const int r = kb * 32 + col;
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) {
+                const u32x4 kv = sk[r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                s[kb] = TR::mma32(__builtin_bit_cast(v8, kv), qf[ks], s[kb]);
+            }
+        }
+
+        // masking: causal prefix, ragged tail, key padding -> -inf
+        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    bool vis = key < N;
+                    if (p.causal) vis = vis && key <= qi;
+                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    if (!vis) s[kb][j] = -INFINITY;
+                }
+            }
+        }
+
+        // running maximum
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+        mt = xhalf_max(mt);
+        const float m_new = fmaxf(m, mt);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2((m - m_ref) * c);     // 0 when m = -inf
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        const float mc = m_ref * c;
+
+        // P = exp2(s*c - m*c), rounded to T; the rounded values feed both P.V
+        // and the running sum, so the output is an exact convex combination.
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS; ++ks2) {
+            const int kb = ks2 >> 1, half = ks2 & 1;
+            v8 pb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const T pv = (T)fast_exp2(fmaf(s[kb][8 * half + i], c, -mc));
+                pb[i] = pv;
+                l += (float)pv;
+            }
+            // V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
+            const int g = (lane >> 4) & 1;
+            const int rsrc = (lane & 15) >> 2, qsrc = lane & 3;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int chunk = db * 4 + 2 * g + (qsrc >> 1);
+                const int row1 = ks2 * 16 + 4 * hh + rsrc;
+                const int row2 = row1 + 8;
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                typedef __attribute__((address_space(3))) char lds_char;
+                lds_char* vbase = (lds_char*)sv;
+                const int off1 = (row1 * CPR + swz_v16<CPR>(row1, chunk)) * 16 + (qsrc & 1) * 8;
+                const int off2 = (row2 * CPR + swz_v16<CPR>(row2, chunk)) * 16 + (qsrc & 1) * 8;
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off1));
+                const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off2));
+                const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
+                const u32x4 w = (u32x4){w1[0], w1[1], w2[0], w2[1]};
+                o[db] = TR::mma32(__builtin_bit_cast(v8, w), pb, o[db]);
+            }
+        }
+    }
+
+    // epilogue: O = acc / l, lse = m*scale + ln(l); empty rows -> (0, -inf)
+    const float lt = xhalf_sum(l);
+    if (qi < N) {
+        const size_t orow = (size_t)bh * N + qi;
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = db * 32 + 8 * g4 + 4 * hh;
+                float x[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = empty ? 0.f : o[db][4 * g4 + r] * inv;
+                if (p.out_f32) {
+                    *(f32x4*)((float*)p.o + orow * D + d0) = (f32x4){x[0], x[1], x[2], x[3]};
+                } else {
+                    typedef __attribute__((ext_vector_type(4))) T t4;
+                    *(t4*)((T*)p.o + orow * D + d0) = (t4){(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
+                }
+            }
+        }
+        if (p.lse && hh == 0)
+            p.lse[orow] = empty ? -INFINITY : fmaf(m, p.scale, __builtin_amdgcn_logf(lt) * 0.69314718055994530942f);
+    }
+}
+
+// ============================================================ fp32, 32x32x2
+template <int D, int BR, int BC>
+__global__ void __launch_bounds__(BR * 2)
+fwd_m32_f32(FwdParams p)
+{
+    constexpr int NW = BR / 32, NT = NW * 64;
+    constexpr int CPR = D * 4 / 16;
+    constexpr int NKB = BC / 32, DB = D / 32, DH = D / 2, DC = D / 8;
+    static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
+
+    __shared__ u32x4 sk[BC * CPR];
+    __shared__ u32x4 sv[BC * CPR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, col = lane & 31;
+    int bh, qt;
+    tile_of_block(p, bh, qt);
+    const int N = p.N;
+    const int b = bh / p.H;
+    const int q0 = qt * BR;
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const float* __restrict__ Q = (const float*)p.q + head;
+    const float* __restrict__ K = (const float*)p.k + head;
+    const float* __restrict__ V = (const float*)p.v + head;
+    const int qi = q0 + wave * 32 + col;
+
+    // Q^T operand of 32x32x2: step t uses d = t + (D/2)*hh
+    float qf[DH];
+#pragma unroll
+    for (int t = 0; t < DC; ++t) {
+        f32x4 w = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (qi < N) w = *(const f32x4*)(Q + (size_t)qi * D + 4 * t + DH * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * t + e] = w[e];
+    }
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+    const int nkt = (N + BC - 1) / BC;
+    int kt_end = nkt;
+    if (p.causal) {
+        const int last_q = min(q0 + BR, N) - 1;
+        kt_end = min(nkt, last_q / BC + 1);
+    }
+    const int wave_q0 = q0 + wave * 32;
+    const float c = p.c;
+    const float* svf = (const float*)sv;
+
+    for (int it = 0; it < kt_end; ++it) {
+        const int kt = p.kv_order ? (kt_end - 1 - it) : it;
+        const int k0 = kt * BC;
+        const int rows_valid = min(BC, N - k0);
+        __syncthreads();
+        stage_tile<BC, CPR, NT, 0>(sk, (const u32x4*)(K + (size_t)k0 * D), rows_valid, tid);
+        stage_tile<BC, CPR, NT, 2>(sv, (const u32x4*)(V + (size_t)k0 * D), rows_valid, tid);
+        __syncthreads();
+
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = (f32x16){};
+            const int r = kb * 32 + col;
+#pragma unroll
+            for (int t = 0; t < DC; ++t) {
+                const f32x4 kv = __builtin_bit_cast(f32x4, sk[r * CPR + swz_k<CPR>(r, t + DC * hh)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], qf[4 * t + e], s[kb], 0, 0, 0);
+            }
+        }
+
+        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    bool vis = key < N;
+                    if (p.causal) vis = vis && key <= qi;
+                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    if (!vis) s[kb][j] = -INFINITY;
+                }
+            }
+        }
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+        mt = xhalf_max(mt);
+        const float m_new = fmaxf(m, mt);
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2((m - m_ref) * c);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        const float mc = m_ref * c;
+
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -mc));
+                l += s[kb][j];
+            }
+            // O^T += V^T P^T, two keys per step: lane hh supplies key 8g+4hh+r
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = kb * 32 + 8 * g + 4 * hh + r;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int dcol = db * 32 + col;
+                        const float a = svf[(row * CPR + swz_v32(row, dcol >> 2)) * 4 + (dcol & 3)];
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][4 * g + r], o[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    const float lt = xhalf_sum(l);
+    if (qi < N) {
+        const size_t orow = (size_t)bh * N + qi;
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = db * 32 + 8 * g4 + 4 * hh;
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = empty ? 0.f : o[db][4 * g4 + r] * inv;
+                *(f32x4*)((float*)p.o + orow * D + d0) = x;
+            }
+        }
+        if (p.lse && hh == 0)
+            p.lse[orow] = empty ? -INFINITY : fmaf(m, p.scale, __builtin_amdgcn_logf(lt) * 0.69314718055994530942f);
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D, int BR, int BC>
+hipError_t launch_h16(const FwdParams& p, hipStream_t st)
+{
+    const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
+    hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
+    return hipGetLastError();
+}
+
+template <int D, int BR, int BC>
+hipError_t launch_f32(const FwdParams& p, hipStream_t st)
+{
+    const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
+    hipLaunchKernelGGL((fwd_m32_f32<D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
+    return hipGetLastError();
+}
+
+// Instance tables, one per input type (defined in the fwd_inst_*.hip files).
+LaunchFn lookup_bf16(int D, int BR, int BC);
+LaunchFn lookup_f16(int D, int BR, int BC);
+LaunchFn lookup_f32(int D, int BR, int BC);
+
+}  // namespace attnk
