@@ -123,3 +123,32 @@ def c2_mask(B: int, N: int, config_id: int = 2) -> np.ndarray:
     if B > 1:
         lengths[1] = 0
     return padding_mask(B, N, config_id, lengths)
+
+
+def to_torch(arr: np.ndarray, dtype: str, device: str = "cuda"):
+    """Copy stored values to a torch tensor of the storage type (bf16 from its bits)."""
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(device)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(arr, np.float16)).to(device)
+    bits = np.ascontiguousarray(arr, np.uint16).view(np.int16)
+    return torch.from_numpy(bits).to(device).view(torch.bfloat16)
+
+
+def upload(p: QKV, device: str = "cuda"):
+    """(q, k, v) of a problem as device tensors."""
+    return to_torch(p.q, p.dtype, device), to_torch(p.k, p.dtype, device), to_torch(p.v, p.dtype, device)
+
+
+def sample_rows(B: int, H: int, N: int, per_head: int = 24, seed: int = 0) -> np.ndarray:
+    """Flat row indices (b*H + h)*N + i for checks at full size: for every
+    (b, h) the first rows, the rows around the first 32-row boundary, the middle
+    and last rows, plus `per_head` rows drawn uniformly."""
+    rng = np.random.default_rng([4242, B, H, N, seed])
+    rows = []
+    for bh in range(B * H):
+        pick = {0, 1, min(31, N - 1), min(32, N - 1), N // 2, max(N - 2, 0), N - 1}
+        pick.update(int(x) for x in rng.integers(0, N, size=per_head))
+        rows.extend(bh * N + i for i in sorted(pick) if 0 <= i < N)
+    return np.array(rows, np.int64)

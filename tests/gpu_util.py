@@ -21,18 +21,9 @@ def half_ulp(x, dtype):
     return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - mant)
 
 
-def to_torch(arr, dtype, device="cuda"):
-    import torch
-    if dtype == "f32":
-        return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(device)
-    if dtype == "f16":
-        return torch.from_numpy(np.ascontiguousarray(arr, np.float16)).to(device)
-    bits = np.ascontiguousarray(arr, np.uint16).view(np.int16)
-    return torch.from_numpy(bits).to(device).view(torch.bfloat16)
-
-
-def upload(p: synth.QKV):
-    return to_torch(p.q, p.dtype), to_torch(p.k, p.dtype), to_torch(p.v, p.dtype)
+to_torch = synth.to_torch
+upload = synth.upload
+sample_rows = synth.sample_rows
 
 
 def mask_to_torch(mask):
@@ -43,19 +34,6 @@ def mask_to_torch(mask):
 def host(t):
     import torch
     return t.detach().to(torch.float64).cpu().numpy()
-
-
-def sample_rows(B, H, N, per_head=24, seed=0):
-    """Flat row indices (b*H+h)*N + i: for every (b, h) the first and last rows,
-    plus rows spread over the sequence (including every query-tile boundary
-    region), for the checks at full size."""
-    rng = np.random.default_rng([4242, B, H, N, seed])
-    rows = []
-    for bh in range(B * H):
-        pick = {0, 1, min(31, N - 1), min(32, N - 1), N // 2, N - 2 if N > 1 else 0, N - 1}
-        pick.update(int(x) for x in rng.integers(0, N, size=per_head))
-        rows.extend(bh * N + i for i in sorted(pick) if 0 <= i < N)
-    return np.array(rows, np.int64)
 
 
 def max_abs(a, b):
