@@ -156,19 +156,103 @@ __device__ __forceinline__ void tile_of_block(const FwdParams& p, int& bh, int& 
 }
 
 // ============================================================ 16-bit, 32x32
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (vmcnt only; LDS and scalar counters untouched).
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for the in-flight tile prefetches).  The empty asm statements keep
+// the compiler from moving memory operations across it; LDS reads before it
+// have all been consumed, LDS DMA writes are waited for explicitly.
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave instruction of LDS DMA: lane L copies 16 bytes from its global
+// address to LDS byte address lds_base + 16*L (lds_base is wave-uniform and
+// goes through M0, which is saved and restored around the copy).  Written as
+// inline asm so that the compiler does not treat the copy as an LDS store it
+// must wait for before every later LDS read: completion is tracked explicitly
+// with wait_vmcnt() and a barrier.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
+
+// Issue the asynchronous copy of one BC-row tile (rows k0.., row stride D
+// elements of 2 bytes) straight into LDS with global_load_lds_dwordx4.  Each
+// wave instruction fills 64 consecutive 16-byte LDS slots; slot p holds row
+// p / CPR, logical chunk (p % CPR) ^ f(row), so the lane that owns slot p
+// fetches that logical chunk.  Rows past the end are clamped to row N-1: every
+// load stays in bounds and the padding keys (masked to -inf) carry finite data.
+template <int BC, int CPR, int NW, int KIND, typename T>
+__device__ __forceinline__ void issue_tile(u32x4* lds_tile, const T* __restrict__ g, int k0, int N,
+                                           int wave, int lane)
+{
+    constexpr int CH = BC * CPR;
+    constexpr int NI = CH / (64 * NW);
+    static_assert(NI >= 1 && CH % (64 * NW) == 0, "tile too small for the workgroup");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int p0 = (wave * NI + i) * 64;
+        const int pch = p0 + lane;
+        const int r = pch / CPR, pc = pch % CPR;
+        const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : swz_v16<CPR>(r, pc);
+        const int grow = min(k0 + r, N - 1);
+        const T* src = g + (size_t)grow * (CPR * 8) + c * 8;
+        lds_dma16((const void*)src, lds_addr(lds_tile + p0));
+    }
+}
+
+template <typename T> struct Dot2;
+template <> struct Dot2<__bf16> {
+    typedef __attribute__((ext_vector_type(2))) __bf16 v2;
+    static __device__ __forceinline__ float sum2(v2 a, float acc)
+    { return __builtin_amdgcn_fdot2_f32_bf16(a, (v2){(__bf16)1.0f, (__bf16)1.0f}, acc, false); }
+};
+template <> struct Dot2<_Float16> {
+    typedef __attribute__((ext_vector_type(2))) _Float16 v2;
+    static __device__ __forceinline__ float sum2(v2 a, float acc)
+    { return __builtin_amdgcn_fdot2(a, (v2){(_Float16)1.0f, (_Float16)1.0f}, acc, false); }
+};
+
+// Waves per SIMD the 16-bit kernel is register-budgeted for: two for the
+// tiles whose state fits in 256 registers, one otherwise.
+template <int D, int BC> struct H16Occ { static constexpr int value = (D * BC <= 128 * 64) ? 2 : 1; };
+
 template <typename T, int D, int BR, int BC>
-__global__ void __launch_bounds__(BR * 2)
+__global__ void __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(H16Occ<D, BC>::value)))
 fwd_m32_h16(FwdParams p)
 {
     using TR = H16<T>;
     using v8 = typename TR::v8;
-    constexpr int NW = BR / 32, NT = NW * 64;
+    using v2 = typename Dot2<T>::v2;
+    constexpr int NW = BR / 32;
     constexpr int CPR = D * 2 / 16;            // 16-byte chunks per row
     constexpr int NKB = BC / 32, DK = D / 16, DB = D / 32, KS = BC / 16;
+    constexpr int NI = BC * CPR / (64 * NW);   // DMA instructions per wave per tile
     static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
 
-    __shared__ u32x4 sk[BC * CPR];
-    __shared__ u32x4 sv[BC * CPR];
+    __shared__ u32x4 sk[2][BC * CPR];
+    __shared__ u32x4 sv[2][BC * CPR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, col = lane & 31;
@@ -183,14 +267,28 @@ fwd_m32_h16(FwdParams p)
     const T* __restrict__ V = (const T*)p.v + head;
     const int qi = q0 + wave * 32 + col;       // this lane's query row
 
-    // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7]
+    const int nkt = (N + BC - 1) / BC;
+    int kt_end = nkt;
+    if (p.causal) kt_end = min(nkt, (min(q0 + BR, N) - 1) / BC + 1);
+    const int order = p.kv_order;
+    auto tile_at = [&](int it) { return order ? (kt_end - 1 - it) : it; };
+
+    // prologue: first K and V tiles in flight before Q is even loaded
+    issue_tile<BC, CPR, NW, 0>(sk[0], K, tile_at(0) * BC, N, wave, lane);
+    issue_tile<BC, CPR, NW, 1>(sv[0], V, tile_at(0) * BC, N, wave, lane);
+
+    // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7].  The empty asm
+    // consumes it here, so the compiler's wait for these loads sits before the
+    // loop and not inside it (where it would also drain the tile prefetches).
+    u32x4 qw[DK];
+    const int qrow = min(qi, N - 1);
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) qw[ks] = *(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8);
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(qw[ks]));
     v8 qf[DK];
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-        u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-        if (qi < N) w = *(const u32x4*)(Q + (size_t)qi * D + ks * 16 + hh * 8);
-        qf[ks] = __builtin_bit_cast(v8, w);
-    }
+    for (int ks = 0; ks < DK; ++ks) qf[ks] = __builtin_bit_cast(v8, qw[ks]);
 
     float m = -INFINITY;       // running raw maximum of q.k over visible keys
     float l = 0.f;             // this lane's share of the running sum
@@ -198,23 +296,21 @@ fwd_m32_h16(FwdParams p)
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 
-    const int nkt = (N + BC - 1) / BC;
-    int kt_end = nkt;
-    if (p.causal) {
-        const int last_q = min(q0 + BR, N) - 1;
-        kt_end = min(nkt, last_q / BC + 1);
-    }
     const int wave_q0 = q0 + wave * 32;
     const float c = p.c;
+    const int g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
 
     for (int it = 0; it < kt_end; ++it) {
-        const int kt = p.kv_order ? (kt_end - 1 - it) : it;
-        const int k0 = kt * BC;
-        const int rows_valid = min(BC, N - k0);
-        __syncthreads();
-        stage_tile<BC, CPR, NT, 0>(sk, (const u32x4*)(K + (size_t)k0 * D), rows_valid, tid);
-        stage_tile<BC, CPR, NT, 1>(sv, (const u32x4*)(V + (size_t)k0 * D), rows_valid, tid);
-        __syncthreads();
+        const int buf = it & 1;
+        const int k0 = tile_at(it) * BC;
+        const bool has_next = it + 1 < kt_end;
+
+        // K(it) landed (V(it) may still be in flight); everyone done with buf^1
+        wait_vmcnt<NI>();
+        wg_barrier();
+        if (has_next) issue_tile<BC, CPR, NW, 0>(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave, lane);
 
         // S^T = K Q^T : 32 keys x 32 queries per block
         f32x16 s[NKB];
@@ -224,7 +320,7 @@ fwd_m32_h16(FwdParams p)
             const int r = kb * 32 + col;
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
-                const u32x4 kv = sk[r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                const u32x4 kv = sk[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
                 s[kb] = TR::mma32(__builtin_bit_cast(v8, kv), qf[ks], s[kb]);
             }
         }
@@ -232,20 +328,32 @@ fwd_m32_h16(FwdParams p)
         // masking: causal prefix, ragged tail, key padding -> -inf
         const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
         if (need_mask) {
+            if (p.mask) {
+                const uint8_t* mrow = p.mask + (size_t)b * N;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    uint8_t pad[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        pad[j] = mrow[min(k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3), N - 1)];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (pad[j]) s[kb][j] = -INFINITY;
+                }
+            }
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    bool vis = key < N;
-                    if (p.causal) vis = vis && key <= qi;
-                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    const bool vis = key < N && (!p.causal || key <= qi);
                     if (!vis) s[kb][j] = -INFINITY;
                 }
             }
         }
 
-        // running maximum
+        // running maximum; the O rescale is skipped when no row of the wave
+        // changed its maximum (alpha == 1 exactly)
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -257,40 +365,51 @@ fwd_m32_h16(FwdParams p)
         const float alpha = fast_exp2((m - m_ref) * c);     // 0 when m = -inf
         m = m_new;
         l *= alpha;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
         const float mc = m_ref * c;
 
-        // P = exp2(s*c - m*c), rounded to T; the rounded values feed both P.V
-        // and the running sum, so the output is an exact convex combination.
+        // P = exp2(s*c - m*c) rounded to T; the rounded values feed both P.V
+        // and the running sum (v_dot2 with (1, 1)), so the output is an exact
+        // convex combination of value rows.
+        v8 pb[KS];
 #pragma unroll
         for (int ks2 = 0; ks2 < KS; ++ks2) {
             const int kb = ks2 >> 1, half = ks2 & 1;
-            v8 pb;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const T pv = (T)fast_exp2(fmaf(s[kb][8 * half + i], c, -mc));
-                pb[i] = pv;
-                l += (float)pv;
+            for (int i = 0; i < 8; i += 2) {
+                const float x0 = fast_exp2(fmaf(s[kb][8 * half + i], c, -mc));
+                const float x1 = fast_exp2(fmaf(s[kb][8 * half + i + 1], c, -mc));
+                const v2 pr = (v2){(T)x0, (T)x1};
+                pb[ks2][i] = pr[0];
+                pb[ks2][i + 1] = pr[1];
+                l = Dot2<T>::sum2(pr, l);
             }
-            // V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
-            const int g = (lane >> 4) & 1;
-            const int rsrc = (lane & 15) >> 2, qsrc = lane & 3;
+        }
+
+        // V(it) landed; everyone done with V buf^1
+        if (has_next) wait_vmcnt<NI>(); else wait_vmcnt<0>();
+        wg_barrier();
+        if (has_next) issue_tile<BC, CPR, NW, 1>(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave, lane);
+
+        // O^T += V^T P^T; V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
+        lds_char* vbase = (lds_char*)sv[buf];
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS; ++ks2) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int chunk = db * 4 + 2 * g + (qsrc >> 1);
                 const int row1 = ks2 * 16 + 4 * hh + rsrc;
                 const int row2 = row1 + 8;
-                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                typedef __attribute__((address_space(3))) char lds_char;
-                lds_char* vbase = (lds_char*)sv;
                 const int off1 = (row1 * CPR + swz_v16<CPR>(row1, chunk)) * 16 + (qsrc & 1) * 8;
                 const int off2 = (row2 * CPR + swz_v16<CPR>(row2, chunk)) * 16 + (qsrc & 1) * 8;
                 const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off1));
                 const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off2));
                 const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
                 const u32x4 w = (u32x4){w1[0], w1[1], w2[0], w2[1]};
-                o[db] = TR::mma32(__builtin_bit_cast(v8, w), pb, o[db]);
+                o[db] = TR::mma32(__builtin_bit_cast(v8, w), pb[ks2], o[db]);
             }
         }
     }
