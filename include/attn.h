@@ -80,7 +80,8 @@ enum attn_status {
 };
 
 /* Tile and fold-order options (attn_fwd_ex).
- *   br: query rows per workgroup tile, one of 16, 32, 64, 128 (0 = default).
+ *   br: query rows per workgroup tile, one of 16, 32, 64, 128, or 256 for the
+ *       16-bit types with bc <= 64 at d = 128 or bc = 64 at d = 64 (0 = default).
  *   bc: keys per key tile, one of 16, 32, 64, 128 (0 = default).  bc is also the
  *       rescaling granularity: the running maximum is updated once per tile.
  *   kv_order: 0 folds each row's key tiles first to last, 1 last to first.

@@ -35,7 +35,8 @@ def test_version_and_status_strings():
 
 
 def test_default_tiles():
-    assert A.default_tiles(A.BF16, 128, True) == (128, 64)
+    assert A.default_tiles(A.BF16, 128, True) == (256, 64)
+    assert A.default_tiles(A.F32, 64, False) == (128, 64)
     with pytest.raises(A.AttnError):
         A.default_tiles(A.BF16, 96)
     with pytest.raises(A.AttnError):
@@ -70,6 +71,7 @@ def test_rejections():
     assert chk(dtype=5) == DTYPE and chk(dtype=-1) == DTYPE
     assert chk(q=0x10008) == ALIGN and chk(lse=0x50002) == ALIGN
     assert chk(br=48) == TILE and chk(bc=256) == TILE and chk(kv_order=2) == TILE
+    assert chk(br=256, bc=128) == TILE and chk(br=256, dtype=A.F32) == TILE      # not compiled
     for bad in (0.0, -0.125, float("inf"), float("nan")):
         assert chk(scale=bad) == SCALE
     assert chk(o=0x10000 + 16) == ALIAS                     # o inside q

@@ -158,9 +158,10 @@ def test_key_zero_padded_under_causal_masks_exactly_row_zero(attn):
 
 # ------------------------------------------------------------------ tiles
 TILES = [(br, bc) for br in (32, 64, 128) for bc in (32, 64, 128)]
+WIDE_TILES = [(256, 32), (256, 64)]      # eight-wave tiles, 16-bit inputs only
 
 
-@pytest.mark.parametrize("br,bc", TILES)
+@pytest.mark.parametrize("br,bc", TILES + WIDE_TILES)
 def test_tile_shapes_and_orders_bf16(attn, br, bc):
     """Every tile shape and both fold orders, on a ragged length (1000, not a
     multiple of any tile) with peaked rows (Q, K scaled by 4), d = 128."""

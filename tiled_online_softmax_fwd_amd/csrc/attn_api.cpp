@@ -43,13 +43,15 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 }
 
 bool valid_tile(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
+bool valid_br(int t) { return valid_tile(t) || t == 256; }
 
-// Defaults per (input type, head size): 128 query rows per workgroup (four
-// waves of 32 rows), 64 keys per tile.
+// Defaults per input type: 16-bit inputs use 256 query rows per workgroup
+// (eight waves of 32 rows, sharing each K/V tile) and 64 keys per tile; fp32
+// uses 128 rows (its tiles are twice as large in LDS).
 void defaults(int dtype, int d, int causal, int* br, int* bc)
 {
-    (void)dtype; (void)d; (void)causal;
-    *br = 128;
+    (void)d; (void)causal;
+    *br = dtype == ATTN_F32 ? 128 : 256;
     *bc = 64;
 }
 
@@ -103,7 +105,7 @@ int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, i
     for (int i = 0; i < 5; ++i)
         if (opts->reserved[i] != 0) return fail(ATTN_ERR_TILE, "attn_opts.reserved[%d] must be 0", i);
     if (opts->br != 0) {
-        if (!valid_tile(opts->br)) return fail(ATTN_ERR_TILE, "br=%d not in {16,32,64,128}", opts->br);
+        if (!valid_br(opts->br)) return fail(ATTN_ERR_TILE, "br=%d not in {16,32,64,128,256}", opts->br);
         *br = opts->br;
     }
     if (opts->bc != 0) {

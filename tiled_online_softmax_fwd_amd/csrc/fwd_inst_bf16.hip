@@ -8,6 +8,8 @@ LaunchFn lookup_bf16(int D, int BR, int BC)
 #define X(d, br, bc) if (D == d && BR == br && BC == bc) return &launch_h16<__bf16, d, br, bc>;
     ATTN_FWD_TILES(X, 64)
     ATTN_FWD_TILES(X, 128)
+    ATTN_FWD_TILES_WIDE_64(X)
+    ATTN_FWD_TILES_WIDE_128(X)
 #undef X
     return nullptr;
 }

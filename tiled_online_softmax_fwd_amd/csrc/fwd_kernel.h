@@ -177,50 +177,79 @@ __device__ __forceinline__ void wg_barrier()
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One wave instruction of LDS DMA: lane L copies 16 bytes from its global
-// address to LDS byte address lds_base + 16*L (lds_base is wave-uniform and
-// goes through M0, which is saved and restored around the copy).  Written as
-// inline asm so that the compiler does not treat the copy as an LDS store it
-// must wait for before every later LDS read: completion is tracked explicitly
-// with wait_vmcnt() and a barrier.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base)
+// One wave instruction of LDS DMA: lane L copies 16 bytes from global address
+// gbase + voff(L) to LDS byte address lds_base + 16*L.  gbase and lds_base are
+// wave-uniform (SGPRs; lds_base goes through M0, which is saved and restored).
+// Written as inline asm so that the compiler does not treat the copy as an LDS
+// store it must wait for before every later LDS read: completion is tracked
+// explicitly with wait_vmcnt() and a barrier.
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void lds_dma16(uint64_t gbase, uint32_t voff, uint32_t lds_base)
 {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %2\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %3\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
                  "s_mov_b32 m0, %0"
                  : "=&s"(saved)
-                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
 
-// Issue the asynchronous copy of one BC-row tile (rows k0.., row stride D
-// elements of 2 bytes) straight into LDS with global_load_lds_dwordx4.  Each
-// wave instruction fills 64 consecutive 16-byte LDS slots; slot p holds row
-// p / CPR, logical chunk (p % CPR) ^ f(row), so the lane that owns slot p
-// fetches that logical chunk.  Rows past the end are clamped to row N-1: every
-// load stays in bounds and the padding keys (masked to -inf) carry finite data.
-template <int BC, int CPR, int NW, int KIND, typename T>
-__device__ __forceinline__ void issue_tile(u32x4* lds_tile, const T* __restrict__ g, int k0, int N,
-                                           int wave, int lane)
-{
-    constexpr int CH = BC * CPR;
-    constexpr int NI = CH / (64 * NW);
+// Copy plan of one BC-row tile (row stride CPR 16-byte chunks) into LDS with
+// global_load_lds_dwordx4.  Each wave instruction i fills the 64 consecutive
+// 16-byte LDS slots starting at p0 = (wave*NI + i)*64; slot p holds row p/CPR,
+// logical chunk (p % CPR) ^ f(row), so the lane that owns slot p fetches that
+// chunk.  The per-lane byte offsets within a tile are fixed and computed once;
+// per tile only the uniform base pointer moves.  In the last tile rows past
+// the end are clamped to row N-1, so every load stays in bounds and padding
+// keys (masked to -inf) carry finite data.
+template <int BC, int CPR, int NW, int KIND>
+struct TilePlan {
+    static constexpr int CH = BC * CPR;
+    static constexpr int NI = CH / (64 * NW);
     static_assert(NI >= 1 && CH % (64 * NW) == 0, "tile too small for the workgroup");
+    uint32_t off[NI];   // byte offset of this lane's chunk, relative to the tile's row 0
+    int row[NI];        // tile row this lane fetches
+
+    __device__ __forceinline__ void init(int wave, int lane)
+    {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int p0 = (wave * NI + i) * 64;
-        const int pch = p0 + lane;
-        const int r = pch / CPR, pc = pch % CPR;
-        const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : swz_v16<CPR>(r, pc);
-        const int grow = min(k0 + r, N - 1);
-        const T* src = g + (size_t)grow * (CPR * 8) + c * 8;
-        lds_dma16((const void*)src, lds_addr(lds_tile + p0));
+        for (int i = 0; i < NI; ++i) {
+            const int p = (wave * NI + i) * 64 + lane;
+            const int r = p / CPR, pc = p % CPR;
+            const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : swz_v16<CPR>(r, pc);
+            row[i] = r;
+            off[i] = (uint32_t)(r * CPR + c) * 16u;
+        }
     }
-}
+
+    template <typename T>
+    __device__ __forceinline__ void issue(u32x4* lds_tile, const T* g, int k0, int N, int wave) const
+    {
+        const uint64_t gb = uniform_ptr(g + (size_t)k0 * (CPR * 8));
+        const uint32_t lb = lds_addr(lds_tile);
+        if (k0 + BC <= N) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) lds_dma16(gb, off[i], lb + (uint32_t)((wave * NI + i) * 64 * 16));
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int over = max(k0 + row[i] - (N - 1), 0);     // rows past N-1 -> N-1
+                lds_dma16(gb, off[i] - (uint32_t)(over * CPR * 16), lb + (uint32_t)((wave * NI + i) * 64 * 16));
+            }
+        }
+    }
+};
 
 template <typename T> struct Dot2;
 template <> struct Dot2<__bf16> {
@@ -248,13 +277,15 @@ fwd_m32_h16(FwdParams p)
     constexpr int NW = BR / 32;
     constexpr int CPR = D * 2 / 16;            // 16-byte chunks per row
     constexpr int NKB = BC / 32, DK = D / 16, DB = D / 32, KS = BC / 16;
-    constexpr int NI = BC * CPR / (64 * NW);   // DMA instructions per wave per tile
+    using KPlan = TilePlan<BC, CPR, NW, 0>;
+    using VPlan = TilePlan<BC, CPR, NW, 1>;
     static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
 
     __shared__ u32x4 sk[2][BC * CPR];
     __shared__ u32x4 sv[2][BC * CPR];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const int hh = lane >> 5, col = lane & 31;
     int bh, qt;
     tile_of_block(p, bh, qt);
@@ -274,8 +305,12 @@ fwd_m32_h16(FwdParams p)
     auto tile_at = [&](int it) { return order ? (kt_end - 1 - it) : it; };
 
     // prologue: first K and V tiles in flight before Q is even loaded
-    issue_tile<BC, CPR, NW, 0>(sk[0], K, tile_at(0) * BC, N, wave, lane);
-    issue_tile<BC, CPR, NW, 1>(sv[0], V, tile_at(0) * BC, N, wave, lane);
+    KPlan kplan;
+    VPlan vplan;
+    kplan.init(wave, lane);
+    vplan.init(wave, lane);
+    kplan.issue(sk[0], K, tile_at(0) * BC, N, wave);
+    vplan.issue(sv[0], V, tile_at(0) * BC, N, wave);
 
     // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7].  The empty asm
     // consumes it here, so the compiler's wait for these loads sits before the
@@ -307,10 +342,14 @@ fwd_m32_h16(FwdParams p)
         const int k0 = tile_at(it) * BC;
         const bool has_next = it + 1 < kt_end;
 
-        // K(it) landed (V(it) may still be in flight); everyone done with buf^1
-        wait_vmcnt<NI>();
+        // K(it) and V(it) landed (issued one iteration ago); every wave is done
+        // with buffer buf^1, so the next tile can stream into it now
+        wait_vmcnt<0>();
         wg_barrier();
-        if (has_next) issue_tile<BC, CPR, NW, 0>(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave, lane);
+        if (has_next) {
+            kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
+            vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
+        }
 
         // S^T = K Q^T : 32 keys x 32 queries per block
         f32x16 s[NKB];
@@ -389,10 +428,6 @@ fwd_m32_h16(FwdParams p)
             }
         }
 
-        // V(it) landed; everyone done with V buf^1
-        if (has_next) wait_vmcnt<NI>(); else wait_vmcnt<0>();
-        wg_barrier();
-        if (has_next) issue_tile<BC, CPR, NW, 1>(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave, lane);
 
         // O^T += V^T P^T; V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
         lds_char* vbase = (lds_char*)sv[buf];
