@@ -60,8 +60,8 @@ def flops(B, H, N, d, causal):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--B", type=int, default=1)
     ap.add_argument("--H", type=int, default=32)
     ap.add_argument("--N", type=int, default=8192)

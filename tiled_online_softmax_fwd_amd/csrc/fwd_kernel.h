@@ -56,6 +56,9 @@ struct FwdParams {
 
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
 
+// compile-time index (selects the LDS buffer of an unrolled loop body)
+template <int V> struct Int { static constexpr int value = V; };
+
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -281,6 +284,8 @@ fwd_m32_h16(FwdParams p)
     using VPlan = TilePlan<BC, CPR, NW, 1>;
     static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
 
+    // two K/V tile buffers in LDS: the copy of tile it+1 is in flight while
+    // tile it is computed
     __shared__ u32x4 sk[2][BC * CPR];
     __shared__ u32x4 sv[2][BC * CPR];
 
@@ -337,16 +342,18 @@ fwd_m32_h16(FwdParams p)
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     typedef __attribute__((address_space(3))) char lds_char;
 
-    for (int it = 0; it < kt_end; ++it) {
-        const int buf = it & 1;
+    // One key tile.  BUF (the buffer tile `it` lives in, it & 1) is a
+    // compile-time constant: the loop below is unrolled by two, so every LDS
+    // address is a fixed register plus an immediate offset.
+    auto body = [&](auto BUF, int it) {
+        constexpr int buf = decltype(BUF)::value;
         const int k0 = tile_at(it) * BC;
-        const bool has_next = it + 1 < kt_end;
 
-        // K(it) and V(it) landed (issued one iteration ago); every wave is done
-        // with buffer buf^1, so the next tile can stream into it now
+        // tile it landed; every wave is done with iteration it-1, so the
+        // other buffer can be refilled with tile it+1
         wait_vmcnt<0>();
         wg_barrier();
-        if (has_next) {
+        if (it + 1 < kt_end) {
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
         }
@@ -364,31 +371,32 @@ fwd_m32_h16(FwdParams p)
             }
         }
 
-        // masking: causal prefix, ragged tail, key padding -> -inf
-        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
-        if (need_mask) {
-            if (p.mask) {
-                const uint8_t* mrow = p.mask + (size_t)b * N;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    uint8_t pad[16];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        pad[j] = mrow[min(k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3), N - 1)];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (pad[j]) s[kb][j] = -INFINITY;
-                }
-            }
+        // masking -> -inf.  Accumulator element (kb, j) of this lane is key
+        // k0 + 32*kb + 8*(j/4) + 4*hh + j%4.
+        const bool diag = p.causal && k0 + BC - 1 > wave_q0;
+        const bool tail = k0 + BC > N;
+        if (tail || p.mask) {
+            // ragged last tile or key padding: full visibility test
+            const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    const bool vis = key < N && (!p.causal || key <= qi);
+                    bool vis = key < N && (!p.causal || key <= qi);
+                    if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
                     if (!vis) s[kb][j] = -INFINITY;
                 }
             }
+        } else if (diag) {
+            // tile crossing the causal diagonal: key <= qi, one compare and
+            // one select per element against a per-lane limit
+            const int lim = qi - k0 - 4 * hh;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (kb * 32 + 8 * (j >> 2) + (j & 3) > lim) s[kb][j] = -INFINITY;
         }
 
         // running maximum; the O rescale is skipped when no row of the wave
@@ -428,7 +436,6 @@ fwd_m32_h16(FwdParams p)
             }
         }
 
-
         // O^T += V^T P^T; V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
         lds_char* vbase = (lds_char*)sv[buf];
 #pragma unroll
@@ -447,6 +454,11 @@ fwd_m32_h16(FwdParams p)
                 o[db] = TR::mma32(__builtin_bit_cast(v8, w), pb[ks2], o[db]);
             }
         }
+    };
+
+    for (int it = 0; it < kt_end; it += 2) {
+        body(Int<0>{}, it);
+        if (it + 1 < kt_end) body(Int<1>{}, it + 1);
     }
 
     // epilogue: O = acc / l, lse = m*scale + ln(l); empty rows -> (0, -inf)

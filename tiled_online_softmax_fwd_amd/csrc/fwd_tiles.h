@@ -9,4 +9,4 @@
 // 256-row tiles (eight waves) for the 16-bit kernels only; every wave needs at
 // least one 1 KiB LDS-copy instruction per key tile.
 #define ATTN_FWD_TILES_WIDE_64(X) X(64, 256, 64)
-#define ATTN_FWD_TILES_WIDE_128(X) X(128, 256, 32) X(128, 256, 64)
+#define ATTN_FWD_TILES_WIDE_128(X) X(128, 256, 32) X(128, 256, 64) X(128, 256, 128)
