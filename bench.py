@@ -9,9 +9,10 @@ in HBM before timing starts.
 
 Prints ONE JSON line: throughput in TFLOP/s of algorithmic work
 (4*B*H*N^2*d, halved for causal), the roofline of the kernel (HIP-event
-duration per launch against the bf16 matrix-core peak), max |delta| against
-the fp64 oracle on sampled rows, and the oracle's own throughput on the host
-cores on a bounded sample of the same workload.
+duration per launch against the bf16 matrix-core peak), and the fp64 oracle
+timed on the host cores on a bounded row sample of the same workload; the
+sampled rows also give max/mean/std |delta| of the timed launch's output
+against the fp64 definition.
 """
 import argparse
 import hashlib
@@ -73,7 +74,7 @@ def main():
     ap.add_argument("--kv-order", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
-    ap.add_argument("--no-check", action="store_true", help="skip the sampled-row oracle check")
+    ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
     ap.add_argument("--naive", action="store_true", help="also time the materialising baseline")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter calibration)")
@@ -143,20 +144,6 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean {kms.mean():.4f} ms "
           f"(median {np.median(kms):.4f}, min {kms.min():.4f})", file=sys.stderr, flush=True)
 
-    # numerical check of the timed launch: sampled rows against the fp64 oracle
-    check = None
-    if not args.no_check:
-        import oracle
-        rows = synth.sample_rows(B, H, N, per_head=8)
-        o_host = out.to(torch.float64).cpu().numpy().reshape(-1, d)[rows]
-        l_host = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
-        ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, causal)
-        err = np.abs(o_host - ro)
-        fin = np.isfinite(rl)
-        check = {"rows": int(rows.size), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
-                 "std_abs": float(err.std()), "lse_max_abs": float(np.abs(l_host[fin] - rl[fin]).max()),
-                 "output": args.dtype}
-
     naive = None
     if args.naive:
         need = A.lib().attn_naive_workspace_bytes(B, H, N, {"bf16": A.BF16, "f16": A.F16, "f32": A.F32}[args.dtype])
@@ -174,8 +161,11 @@ def main():
         naive = {"ms": nms, "tflops": fl / (nms * 1e-3) / 1e12, "workspace_bytes": int(need)}
         del ws
 
-    # cpu_baseline: the oracle on a bounded row sample of the same workload
+    # cpu_baseline: the oracle on a bounded row sample of the same workload.  The
+    # rows it computes are also compared with the output of the last timed launch
+    # (max, mean and std of |delta| against the fp64 definition).
     cpu = None
+    check = None
     if not args.no_cpu:
         import oracle
         threads = oracle.num_threads()
@@ -189,17 +179,24 @@ def main():
         def time_rows(nr):
             rows = np.sort(rng.choice(B * H * N, size=nr, replace=False))
             t = time.perf_counter()
-            oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, causal)
-            return time.perf_counter() - t, row_flops(rows), nr
+            ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, causal)
+            return time.perf_counter() - t, row_flops(rows), rows, ro, rl
 
-        dt, f, nr = time_rows(min(B * H * N, 256))
+        dt, f, rows, _, _ = time_rows(min(B * H * N, 256))
         rate = f / max(dt, 1e-6)
         target = int(min(B * H * N, max(256, args.cpu_seconds * rate / (4.0 * d * (N / 2 if causal else N)))))
         print(f"[bench] cpu_baseline: {threads} threads, sampling {target} rows", file=sys.stderr, flush=True)
-        dt, f, nr = time_rows(target)
+        dt, f, rows, ro, rl = time_rows(target)
         cpu = {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"{nr} uniformly drawn query rows of B{B} H{H} N{N} d{d} {'causal' if causal else 'full'} "
-                         f"(fp64 plain definition, {dt:.1f} s)"}
+               "sample": f"{rows.size} uniformly drawn query rows of B{B} H{H} N{N} d{d} "
+                         f"{'causal' if causal else 'full'} (fp64 plain definition, {dt:.1f} s)"}
+        o_host = out.to(torch.float64).cpu().numpy().reshape(-1, d)[rows]
+        l_host = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
+        err = np.abs(o_host - ro)
+        fin = np.isfinite(rl)
+        check = {"rows": int(rows.size), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                 "std_abs": float(err.std()), "lse_max_abs": float(np.abs(l_host[fin] - rl[fin]).max()),
+                 "output": args.dtype}
 
     wk = f"B{B}_H{H}_N{N}_d{d}_{args.dtype}_{'causal' if causal else 'full'}_br{br}_bc{bc}"
     tr = traffic_record(wk)

@@ -57,10 +57,15 @@ def test_valid_arguments_pass():
     assert chk() == OK
     assert chk(dtype=A.F32) == OK and chk(dtype=A.F16_OUT_F32) == OK and chk(d=128) == OK
     assert chk(lse=None) == OK
-    for br in (32, 64, 128):
-        for bc in (32, 64, 128):
-            for order in (0, 1):
-                assert chk(br=br, bc=bc, kv_order=order) == OK
+    for dtype in (A.F32, A.F16, A.BF16, A.F16_OUT_F32, A.BF16_OUT_F32):
+        for d in (64, 128):
+            for br in (16, 32, 64, 128):
+                for bc in (16, 32, 64, 128):
+                    for order in (0, 1):
+                        assert chk(dtype=dtype, d=d, br=br, bc=bc, kv_order=order) == OK
+    for bc in (32, 64, 128):
+        assert chk(dtype=A.BF16, d=128, br=256, bc=bc) == OK
+    assert chk(dtype=A.F16, d=64, br=256, bc=64) == OK
 
 
 def test_rejections():

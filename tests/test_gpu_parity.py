@@ -157,8 +157,8 @@ def test_key_zero_padded_under_causal_masks_exactly_row_zero(attn):
 
 
 # ------------------------------------------------------------------ tiles
-TILES = [(br, bc) for br in (32, 64, 128) for bc in (32, 64, 128)]
-WIDE_TILES = [(256, 32), (256, 64)]      # eight-wave tiles, 16-bit inputs only
+TILES = [(br, bc) for br in (16, 32, 64, 128) for bc in (16, 32, 64, 128)]
+WIDE_TILES = [(256, 32), (256, 64), (256, 128)]      # eight-wave tiles, 16-bit inputs only
 
 
 @pytest.mark.parametrize("br,bc", TILES + WIDE_TILES)
@@ -187,6 +187,23 @@ def test_tile_shapes_fp32_causal(attn, br, bc, d):
         o, l = run(attn, p, scale, True, br=br, bc=bc, kv_order=order)
         gu.assert_close(o, ro, gu.TOL_F32, f"fp32 tile {br}x{bc}")
         gu.assert_lse(l, rl, gu.TOL_LSE_F32, "fp32 tile")
+
+
+@pytest.mark.parametrize("br,bc", [(16, 16), (16, 64), (64, 16), (128, 16), (32, 32), (256, 64)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_tiles_16bit_causal_with_padding(attn, br, bc, dtype, d):
+    """Causal + key padding (one sequence with a random valid length, one fully
+    padded) through the 16-row/16-key kernel and the 32-row kernel, ragged N."""
+    N = 300
+    p = synth.make_qkv(4, 2, N, d, dtype, 2)
+    mask = synth.c2_mask(4, N)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    for order in (0, 1):
+        say("tiles causal+padding", dtype, d, br, bc, "order", order)
+        e, o, l, ro, rl = check_full(attn, p, scale, True, mask, f"{dtype} d{d} {br}x{bc} o{order}",
+                                     br=br, bc=bc, kv_order=order)
+        assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
 # ------------------------------------------------------------------ edges

@@ -1,5 +1,6 @@
 // fwd_inst_bf16.hip -- instance table of the bf16 forward kernels.
 #include "fwd_kernel.h"
+#include "fwd_m16.h"
 #include "fwd_tiles.h"
 
 namespace attnk {
@@ -10,6 +11,10 @@ LaunchFn lookup_bf16(int D, int BR, int BC)
     ATTN_FWD_TILES(X, 128)
     ATTN_FWD_TILES_WIDE_64(X)
     ATTN_FWD_TILES_WIDE_128(X)
+#undef X
+#define X(d, br, bc) if (D == d && BR == br && BC == bc) return &launch_m16<__bf16, d, br, bc>;
+    ATTN_FWD_TILES_16(X, 64)
+    ATTN_FWD_TILES_16(X, 128)
 #undef X
     return nullptr;
 }

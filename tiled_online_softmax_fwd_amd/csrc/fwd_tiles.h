@@ -10,3 +10,9 @@
 // least one 1 KiB LDS-copy instruction per key tile.
 #define ATTN_FWD_TILES_WIDE_64(X) X(64, 256, 64)
 #define ATTN_FWD_TILES_WIDE_128(X) X(128, 256, 32) X(128, 256, 64) X(128, 256, 128)
+
+// Tiles with 16 query rows or 16 keys (fwd_m16.h, 16x16 matrix-core shapes),
+// for every input type and head size.
+#define ATTN_FWD_TILES_16(X, D) \
+    X(D, 16, 16)  X(D, 16, 32)  X(D, 16, 64) X(D, 16, 128) \
+    X(D, 32, 16)  X(D, 64, 16)  X(D, 128, 16)
