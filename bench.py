@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (MI355X spec)
 METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak; max|Δ| vs FP64 oracle"
-KERNEL_SOURCES = ["fwd_kernel.h", "fwd_tiles.h", "fwd_inst_bf16.hip"]
+KERNEL_SOURCES = ["fwd_kernel.h"]      # source of the 16-bit forward kernel the bench times
 
 
 def kernel_hash():
