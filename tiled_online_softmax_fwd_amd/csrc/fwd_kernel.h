@@ -2,10 +2,11 @@
 //
 // One workgroup owns BR query rows of one (batch, head) and walks that head's
 // key tiles of BC rows.  Per key tile it (a) stages K and V in LDS, (b) forms
-// the score tile on the matrix cores, (c) updates each query row's running
+// the score tile on the matrix cores, (c) updates each query row's reference
 // maximum m, running sum of exponentials l and unnormalised output acc -- the
 // online merge of the yadro-code tutorial "How FlashAttention reduces GPU
-// memory traffic" (a bigger maximum rescales l and acc by exp(m_old - m_new))
+// memory traffic" (a bigger reference rescales l and acc by exp(m_old - m_new);
+// the reference lags the running maximum by a bounded amount, see ref_step)
 // -- and (d) accumulates P.V on the matrix cores.  acc / l is formed once, at
 // the end.  The score tile lives only in registers: the N x N matrix of Golden
 // et al., "Is Flash Attention Stable?", sec. II-B, is never written anywhere.
@@ -22,8 +23,8 @@
 //
 // Scores are kept raw (q.k) in fp32; the softmax uses base 2 with the factor
 // c = scale * log2(e) folded into one FMA: p = exp2(s*c - m*c).  Masked scores
-// are -inf.  A row whose maximum is still -inf uses 0 as its reference so that
-// no exp2(-inf - -inf) is ever formed.
+// are -inf.  A row with no visible key yet uses 0 as its reference so that no
+// exp2(-inf - -inf) is ever formed.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,6 +77,31 @@ __device__ __forceinline__ float xhalf_sum(float x)
                                               __builtin_bit_cast(unsigned, x), false, false);
     // both halves add (lower + upper) in the same order
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Reference of the online merge.  The merge multiplies l and acc by
+// exp(m_old - m_new) when the reference moves from m_old to m_new; the result
+// acc / l is the same for any reference, as long as no exponent overflows.
+// The reference therefore moves only when a tile's maximum exceeds it by more
+// than REF_SLACK in base-2 units (at the first visible key it always moves),
+// so P <= 2^REF_SLACK and most tiles skip the rescale of acc.  m = -inf means
+// no visible key yet; exponents then use 0 as reference, so exp2(-inf - -inf)
+// is never formed.
+constexpr float REF_SLACK = 8.f;
+struct RefStep {
+    float m;        // new reference (raw q.k units)
+    float mc;       // reference used in the exponents, times c
+    float alpha;    // rescale factor of l and acc (1 when the reference stays)
+    bool moved;
+};
+__device__ __forceinline__ RefStep ref_step(float m, float mt, float c)
+{
+    RefStep r;
+    r.moved = (mt - m) * c > REF_SLACK;    // false for mt = -inf (NaN or -inf compare)
+    r.m = r.moved ? mt : m;
+    r.mc = (r.m == -INFINITY) ? 0.f : r.m * c;
+    r.alpha = r.moved ? fast_exp2((m - r.m) * c) : 1.f;   // 0 when m = -inf
+    return r;
 }
 
 // 16-bit element traits
@@ -330,7 +356,7 @@ fwd_m32_h16(FwdParams p)
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) qf[ks] = __builtin_bit_cast(v8, qw[ks]);
 
-    float m = -INFINITY;       // running raw maximum of q.k over visible keys
+    float m = -INFINITY;       // reference of the merge (raw q.k units), see ref_step
     float l = 0.f;             // this lane's share of the running sum
     f32x16 o[DB];
 #pragma unroll
@@ -399,24 +425,22 @@ fwd_m32_h16(FwdParams p)
                     if (kb * 32 + 8 * (j >> 2) + (j & 3) > lim) s[kb][j] = -INFINITY;
         }
 
-        // running maximum; the O rescale is skipped when no row of the wave
-        // changed its maximum (alpha == 1 exactly)
+        // tile maximum and reference step; the O rescale is skipped when no
+        // row of the wave moved its reference (alpha == 1 exactly)
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
         mt = xhalf_max(mt);
-        const float m_new = fmaxf(m, mt);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_ref) * c);     // 0 when m = -inf
-        m = m_new;
-        l *= alpha;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        const RefStep rs = ref_step(m, mt, c);
+        m = rs.m;
+        l *= rs.alpha;
+        if (__builtin_amdgcn_ballot_w64(rs.moved)) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+            for (int db = 0; db < DB; ++db) o[db] *= rs.alpha;
         }
-        const float mc = m_ref * c;
+        const float mc = rs.mc;
 
         // P = exp2(s*c - m*c) rounded to T; the rounded values feed both P.V
         // and the running sum (v_dot2 with (1, 1)), so the output is an exact
@@ -583,14 +607,14 @@ fwd_m32_f32(FwdParams p)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
         mt = xhalf_max(mt);
-        const float m_new = fmaxf(m, mt);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_ref) * c);
-        m = m_new;
-        l *= alpha;
+        const RefStep rs = ref_step(m, mt, c);
+        m = rs.m;
+        l *= rs.alpha;
+        if (__builtin_amdgcn_ballot_w64(rs.moved)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        const float mc = m_ref * c;
+            for (int db = 0; db < DB; ++db) o[db] *= rs.alpha;
+        }
+        const float mc = rs.mc;
 
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {

@@ -5,8 +5,9 @@
 // Same algorithm as fwd_m32_*: per key tile, the transposed score tile
 // S^T = K Q^T on the matrix cores, a true -inf for invisible keys, the online
 // merge of the yadro-code tutorial "How FlashAttention reduces GPU memory
-// traffic" (running maximum m, running sum l, accumulator rescaled by
-// exp(m_old - m_new)), P.V on the matrix cores, and acc / l once at the end.
+// traffic" (reference m, running sum l, accumulator rescaled by
+// exp(m_old - m_new); see ref_step), P.V on the matrix cores, and acc / l once
+// at the end.
 //
 // Each wave owns 16 query rows.  In the 16x16 accumulator of S^T lane L holds
 // query column L%16 and keys 4*(L/16) + i (i = 0..3) of a 16-key block; those
@@ -186,14 +187,14 @@ fwd_m16(FwdParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
         mt = quad_max(mt);
-        const float m_new = fmaxf(m, mt);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2((m - m_ref) * c);     // 0 while m = -inf
-        m = m_new;
-        l *= alpha;
+        const RefStep rs = ref_step(m, mt, c);
+        m = rs.m;
+        l *= rs.alpha;
+        if (__builtin_amdgcn_ballot_w64(rs.moved)) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        const float mc = m_ref * c;
+            for (int db = 0; db < DB; ++db) o[db] *= rs.alpha;
+        }
+        const float mc = rs.mc;
 
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
