@@ -66,6 +66,11 @@ def test_valid_arguments_pass():
     for bc in (32, 64, 128):
         assert chk(dtype=A.BF16, d=128, br=256, bc=bc) == OK
     assert chk(dtype=A.F16, d=64, br=256, bc=64) == OK
+    # bc alone: the default br falls back to 128 where no 256-row tile exists
+    for dtype in (A.F32, A.BF16):
+        for d in (64, 128):
+            for bc in (16, 32, 64, 128):
+                assert chk(dtype=dtype, d=d, bc=bc) == OK
 
 
 def test_rejections():

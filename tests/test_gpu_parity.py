@@ -156,6 +156,35 @@ def test_key_zero_padded_under_causal_masks_exactly_row_zero(attn):
         assert np.isfinite(l[:, :, 1:]).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_moves_and_stays(attn, dtype, causal):
+    """Rows whose scores rise slowly along the keys (the merge reference moves
+    only every few tiles), steeply (it moves at every tile) or fall (it moves
+    once), plus a random head: the result must equal the plain definition.
+    Scores are exact: q[:, 0] = 1, k[j, 0] = a * j, scale 1.  fp32 gate as for
+    the +1000 shift: 1e-5 + 2 max|v| * 4 ulp(max|s|)."""
+    N, d, H = 1000, 64, 4
+    rng = np.random.default_rng([7, N, 1])
+    q = np.zeros((1, H, N, d)); k = np.zeros((1, H, N, d))
+    v = rng.standard_normal((1, H, N, d))
+    j = np.arange(N)
+    q[0, :3, :, 0] = 1.0
+    for h, a in enumerate((0.01, 0.1, -0.01)):
+        k[0, h, :, 0] = a * j
+    q[0, 3] = rng.standard_normal((N, d)) * 0.2
+    k[0, 3] = rng.standard_normal((N, d))
+    p = synth.qkv_from_f64(q, k, v, dtype)
+    smax = float(np.abs(p.k64[0, :3, :, 0]).max())
+    tol = gu.TOL_H16 if dtype == "bf16" else 1e-5 + 2 * np.abs(p.v64).max() * 4 * 2.0 ** (np.floor(np.log2(smax)) - 23)
+    for bc in (32, 64):
+        say("reference paths", dtype, "causal", causal, "bc", bc)
+        o, l = run(attn, p, 1.0, causal, out_fp32=dtype != "f32", bc=bc)
+        ro, rl = oracle.attn(p.q64, p.k64, p.v64, 1.0, causal)
+        gu.assert_close(o, ro, tol, f"reference paths {dtype} bc{bc}")
+        gu.assert_lse(l, rl, 1e-3 if dtype == "f32" else gu.TOL_LSE_H16, "reference paths")
+
+
 # ------------------------------------------------------------------ tiles
 TILES = [(br, bc) for br in (16, 32, 64, 128) for bc in (16, 32, 64, 128)]
 WIDE_TILES = [(256, 32), (256, 64), (256, 128)]      # eight-wave tiles, 16-bit inputs only

@@ -111,6 +111,8 @@ int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, i
     if (opts->bc != 0) {
         if (!valid_tile(opts->bc)) return fail(ATTN_ERR_TILE, "bc=%d not in {16,32,64,128}", opts->bc);
         *bc = opts->bc;
+        // br left to the library: use 128 rows where the wide tile is not built
+        if (opts->br == 0 && !find(dtype, d, *br, *bc)) *br = 128;
     }
     if (opts->kv_order != 0 && opts->kv_order != 1) return fail(ATTN_ERR_TILE, "kv_order=%d not 0 or 1", opts->kv_order);
     *order = opts->kv_order;
