@@ -72,6 +72,8 @@ def main():
     ap.add_argument("--br", type=int, default=0)
     ap.add_argument("--bc", type=int, default=0)
     ap.add_argument("--kv-order", type=int, default=0)
+    ap.add_argument("--ref-slack", type=int, default=0,
+                    help="lag allowed to the merge reference, base-2 units (0 = exact running maximum)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
@@ -118,7 +120,8 @@ def main():
     bc = args.bc or bc
 
     def step():
-        A.fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, br=br, bc=bc, kv_order=args.kv_order)
+        A.fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, br=br, bc=bc, kv_order=args.kv_order,
+              ref_slack=args.ref_slack)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -199,6 +202,8 @@ def main():
                  "output": args.dtype}
 
     wk = f"B{B}_H{H}_N{N}_d{d}_{args.dtype}_{'causal' if causal else 'full'}_br{br}_bc{bc}"
+    if args.ref_slack:
+        wk += f"_slack{args.ref_slack}"
     tr = traffic_record(wk)
     roof = {"bound": "mfma", "achieved": kernel_tflops, "peak": PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3,
             "unit": "TFLOP/s", "frac": kernel_tflops / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
@@ -220,7 +225,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"B{B} H{H} N{N} d{d} {args.dtype} {'causal' if causal else 'non-causal'} attention forward",
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "br": br, "bc": bc,
-                   "kv_order": args.kv_order, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+                   "kv_order": args.kv_order, "ref_slack": args.ref_slack, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
         "pct_peak": 100.0 * value / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
         "check_vs_fp64_oracle": check,
         "roofline": roof,

@@ -1,8 +1,10 @@
 """Build script for the fp64 CPU oracle (test infrastructure, not product code).
 
-Compiles oracle.c with gcc into liboracle.so next to this file.  No fused
-multiply-add contraction and no fast-math, so the arithmetic is exactly the
-sequence of IEEE double operations the C source spells out.
+Compiles oracle.c (the fp64 oracle) and emulate.c (the precision-emulating
+model of the flash and baseline algorithms) with gcc into liboracle.so next to
+this file.  No fused multiply-add contraction and no fast-math, so the
+arithmetic is exactly the sequence of IEEE double operations the C source
+spells out.
 """
 import os
 import subprocess
@@ -13,11 +15,11 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    src = os.path.join(HERE, "oracle.c")
+    srcs = [os.path.join(HERE, "oracle.c"), os.path.join(HERE, "emulate.c")]
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           src, "-o", tmp, "-lm"]
+           *srcs, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -46,11 +46,11 @@ def test_default_tiles():
 BASE = dict(q=0x10000, k=0x20000, v=0x30000, o=0x40000, lse=0x50000)
 
 
-def chk(B=1, H=2, N=8, d=64, scale=0.125, causal=0, dtype=A.BF16, br=0, bc=0, kv_order=0, **ptrs):
+def chk(B=1, H=2, N=8, d=64, scale=0.125, causal=0, dtype=A.BF16, br=0, bc=0, kv_order=0, ref_slack=0, **ptrs):
     p = dict(BASE)
     p.update(ptrs)
     return A.check_args(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, N, d, scale, causal, None, dtype,
-                        br, bc, kv_order)
+                        br, bc, kv_order, ref_slack)
 
 
 def test_valid_arguments_pass():
@@ -81,6 +81,8 @@ def test_rejections():
     assert chk(dtype=5) == DTYPE and chk(dtype=-1) == DTYPE
     assert chk(q=0x10008) == ALIGN and chk(lse=0x50002) == ALIGN
     assert chk(br=48) == TILE and chk(bc=256) == TILE and chk(kv_order=2) == TILE
+    assert chk(ref_slack=-1) == TILE and chk(ref_slack=16) == TILE
+    assert chk(ref_slack=8) == OK and chk(ref_slack=15) == OK
     assert chk(br=256, bc=128) == TILE and chk(br=256, dtype=A.F32) == TILE      # not compiled
     for bad in (0.0, -0.125, float("inf"), float("nan")):
         assert chk(scale=bad) == SCALE

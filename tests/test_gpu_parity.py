@@ -156,9 +156,10 @@ def test_key_zero_padded_under_causal_masks_exactly_row_zero(attn):
         assert np.isfinite(l[:, :, 1:]).all()
 
 
+@pytest.mark.parametrize("slack", [0, 8])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_reference_moves_and_stays(attn, dtype, causal):
+def test_reference_moves_and_stays(attn, dtype, causal, slack):
     """Rows whose scores rise slowly along the keys (the merge reference moves
     only every few tiles), steeply (it moves at every tile) or fall (it moves
     once), plus a random head: the result must equal the plain definition.
@@ -178,8 +179,8 @@ def test_reference_moves_and_stays(attn, dtype, causal):
     smax = float(np.abs(p.k64[0, :3, :, 0]).max())
     tol = gu.TOL_H16 if dtype == "bf16" else 1e-5 + 2 * np.abs(p.v64).max() * 4 * 2.0 ** (np.floor(np.log2(smax)) - 23)
     for bc in (32, 64):
-        say("reference paths", dtype, "causal", causal, "bc", bc)
-        o, l = run(attn, p, 1.0, causal, out_fp32=dtype != "f32", bc=bc)
+        say("reference paths", dtype, "causal", causal, "bc", bc, "slack", slack)
+        o, l = run(attn, p, 1.0, causal, out_fp32=dtype != "f32", bc=bc, ref_slack=slack)
         ro, rl = oracle.attn(p.q64, p.k64, p.v64, 1.0, causal)
         gu.assert_close(o, ro, tol, f"reference paths {dtype} bc{bc}")
         gu.assert_lse(l, rl, 1e-3 if dtype == "f32" else gu.TOL_LSE_H16, "reference paths")
@@ -325,6 +326,23 @@ def test_c5_headline_shape_sampled_rows(attn):
     """B1 H32 N8192 d128 bf16 causal, default tiles (the launch the benchmark
     times); every head's first, last and spread rows against the oracle."""
     sampled_check(attn, 1, 32, 8192, 128, "bf16", True, 5)
+
+
+def test_c5_with_lagging_reference(attn):
+    """The headline shape with the merge reference allowed to lag by 2^8."""
+    sampled_check(attn, 1, 32, 8192, 128, "bf16", True, 5, per_head=6, ref_slack=8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_c2_with_lagging_reference(attn, dtype):
+    """Causal + key padding with the lagging reference, several tiles."""
+    p = synth.make_qkv(4, 4, 1024, 64, dtype, 2)
+    mask = synth.c2_mask(4, 1024)
+    for br, bc in ((256, 64) if dtype != "f32" else (128, 64), (64, 32), (16, 16)):
+        say("C2 lagging reference", dtype, br, bc)
+        e, o, l, ro, rl = check_full(attn, p, 0.125, True, mask, f"C2 slack {dtype} {br}x{bc}",
+                                     br=br, bc=bc, ref_slack=8)
+        assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
 def test_c3_shape_sampled_rows(attn):

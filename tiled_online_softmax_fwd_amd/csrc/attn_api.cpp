@@ -97,12 +97,13 @@ int check_pointers(const void* q, const void* k, const void* v, void* o, float* 
     return ATTN_OK;
 }
 
-int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, int* bc, int* order)
+int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, int* bc, int* order, int* slack)
 {
     defaults(dtype, d, causal, br, bc);
     *order = 0;
+    *slack = 0;
     if (!opts) return ATTN_OK;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 4; ++i)
         if (opts->reserved[i] != 0) return fail(ATTN_ERR_TILE, "attn_opts.reserved[%d] must be 0", i);
     if (opts->br != 0) {
         if (!valid_br(opts->br)) return fail(ATTN_ERR_TILE, "br=%d not in {16,32,64,128,256}", opts->br);
@@ -116,16 +117,18 @@ int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, i
     }
     if (opts->kv_order != 0 && opts->kv_order != 1) return fail(ATTN_ERR_TILE, "kv_order=%d not 0 or 1", opts->kv_order);
     *order = opts->kv_order;
+    if (opts->ref_slack < 0 || opts->ref_slack > 15) return fail(ATTN_ERR_TILE, "ref_slack=%d not in 0..15", opts->ref_slack);
+    *slack = opts->ref_slack;
     return ATTN_OK;
 }
 
 int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
-              const attn_opts* opts, int* br, int* bc, int* order)
+              const attn_opts* opts, int* br, int* bc, int* order, int* slack)
 {
     int st = check_scalars(B, H, N, d, scale, dtype);
     if (st) return st;
-    st = resolve_opts(dtype, d, causal, opts, br, bc, order);
+    st = resolve_opts(dtype, d, causal, opts, br, bc, order, slack);
     if (st) return st;
     if (!find(dtype, d, *br, *bc))
         return fail(ATTN_ERR_TILE, "no kernel for dtype %d, d=%d, br=%d, bc=%d", dtype, d, *br, *bc);
@@ -142,8 +145,8 @@ int attn_check_args(const void* q, const void* k, const void* v, void* o, float*
                     const uint8_t* key_padding_mask, int dtype, const attn_opts* opts)
 {
     (void)key_padding_mask;
-    int br, bc, order;
-    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order);
+    int br, bc, order, slack;
+    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order, &slack);
     return st ? st : ok();
 }
 
@@ -152,8 +155,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 const uint8_t* key_padding_mask, int dtype, void* stream,
                 const attn_opts* opts)
 {
-    int br, bc, order;
-    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order);
+    int br, bc, order, slack;
+    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order, &slack);
     if (st) return st;
     if ((int64_t)B * H * N == 0) return ok();
 
@@ -165,6 +168,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e), rounded once
     p.causal = causal ? 1 : 0;
     p.kv_order = order;
+    p.slack = (float)slack;
     p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
     const hipError_t e = find(dtype, d, br, bc)(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

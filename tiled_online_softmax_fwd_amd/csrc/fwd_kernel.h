@@ -53,6 +53,7 @@ struct FwdParams {
     int causal;
     int kv_order;          // 0 ascending key tiles, 1 descending
     int out_f32;           // o is float instead of the input type
+    float slack;           // lag allowed to the merge reference (base-2 units, 0 = exact maximum)
 };
 
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
@@ -80,24 +81,24 @@ __device__ __forceinline__ float xhalf_sum(float x)
 }
 
 // Reference of the online merge.  The merge multiplies l and acc by
-// exp(m_old - m_new) when the reference moves from m_old to m_new; the result
-// acc / l is the same for any reference, as long as no exponent overflows.
-// The reference therefore moves only when a tile's maximum exceeds it by more
-// than REF_SLACK in base-2 units (at the first visible key it always moves),
-// so P <= 2^REF_SLACK and most tiles skip the rescale of acc.  m = -inf means
-// no visible key yet; exponents then use 0 as reference, so exp2(-inf - -inf)
-// is never formed.
-constexpr float REF_SLACK = 8.f;
+// exp(m_old - m_new) when the reference moves from m_old to m_new, and the
+// result acc / l (and lse = m + ln l) is the same for any reference as long as
+// no exponent overflows.  With slack 0 the reference is the exact running
+// maximum (it moves whenever a tile's maximum exceeds it).  With slack s > 0 it
+// moves only when a tile's maximum exceeds it by more than s in base-2 units,
+// so P <= 2^s and most tiles skip the rescale of acc.  At the first visible key
+// it always moves.  m = -inf means no visible key yet; exponents then use 0 as
+// reference, so exp2(-inf - -inf) is never formed.
 struct RefStep {
     float m;        // new reference (raw q.k units)
     float mc;       // reference used in the exponents, times c
     float alpha;    // rescale factor of l and acc (1 when the reference stays)
     bool moved;
 };
-__device__ __forceinline__ RefStep ref_step(float m, float mt, float c)
+__device__ __forceinline__ RefStep ref_step(float m, float mt, float c, float slack)
 {
     RefStep r;
-    r.moved = (mt - m) * c > REF_SLACK;    // false for mt = -inf (NaN or -inf compare)
+    r.moved = (mt - m) * c > slack;        // false for mt = -inf (NaN or -inf compare)
     r.m = r.moved ? mt : m;
     r.mc = (r.m == -INFINITY) ? 0.f : r.m * c;
     r.alpha = r.moved ? fast_exp2((m - r.m) * c) : 1.f;   // 0 when m = -inf
@@ -433,7 +434,7 @@ fwd_m32_h16(FwdParams p)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
         mt = xhalf_max(mt);
-        const RefStep rs = ref_step(m, mt, c);
+        const RefStep rs = ref_step(m, mt, c, p.slack);
         m = rs.m;
         l *= rs.alpha;
         if (__builtin_amdgcn_ballot_w64(rs.moved)) {
@@ -607,7 +608,7 @@ fwd_m32_f32(FwdParams p)
 #pragma unroll
             for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
         mt = xhalf_max(mt);
-        const RefStep rs = ref_step(m, mt, c);
+        const RefStep rs = ref_step(m, mt, c, p.slack);
         m = rs.m;
         l *= rs.alpha;
         if (__builtin_amdgcn_ballot_w64(rs.moved)) {

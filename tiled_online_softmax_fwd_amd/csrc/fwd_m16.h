@@ -187,7 +187,7 @@ fwd_m16(FwdParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[kb][i]);
         mt = quad_max(mt);
-        const RefStep rs = ref_step(m, mt, c);
+        const RefStep rs = ref_step(m, mt, c, p.slack);
         m = rs.m;
         l *= rs.alpha;
         if (__builtin_amdgcn_ballot_w64(rs.moved)) {
