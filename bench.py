@@ -78,6 +78,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
     ap.add_argument("--naive", action="store_true", help="also time the materialising baseline")
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode"],
+                    help="prefill: the causal forward (default); decode: Nq query rows against a key/value cache")
+    ap.add_argument("--Nq", type=int, default=1, help="decode: query rows per head")
+    ap.add_argument("--Nk", type=int, default=8192, help="decode: cached keys per head")
+    ap.add_argument("--decode-B", type=int, default=8, help="decode: batch")
+    ap.add_argument("--splits", type=int, default=0, help="decode: key chunks per head (0 = library choice)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (counter calibration)")
     args = ap.parse_args()
@@ -106,6 +112,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
         return
+
+    if args.workload == "decode":
+        return run_decode(args, torch, synth, A)
 
     B, H, N, d = args.B, args.H, args.N, args.d
     causal = not args.no_causal
@@ -233,6 +242,73 @@ def main():
     }
     if naive:
         line["naive_baseline"] = naive
+    print(json.dumps(line), flush=True)
+
+
+def run_decode(args, torch, synth, A):
+    """Key/value-cache decoding: Nq query rows per head against Nk cached keys.
+    Bound by reading K and V once; priced against the HBM bandwidth."""
+    B, H, Nq, Nk, d = args.decode_B, args.H, args.Nq, args.Nk, args.d
+    if args.dtype == "f32":
+        print("the decode path takes 16-bit inputs", file=sys.stderr)
+        sys.exit(2)
+    causal = not args.no_causal
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    print(f"[bench] decode inputs B{B} H{H} Nq{Nq} Nk{Nk} d{d} {args.dtype}", file=sys.stderr, flush=True)
+    kv = synth.make_qkv(B, H, Nk, d, args.dtype, 7)
+    qq = synth.make_qkv(B, H, Nq, d, args.dtype, 7, variant=1)
+    q = synth.to_torch(qq.q, args.dtype)
+    k = synth.to_torch(kv.k, args.dtype)
+    v = synth.to_torch(kv.v, args.dtype)
+    out = torch.empty((B, H, Nq, d), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    need = A.lib().attn_decode_workspace_bytes(B, H, Nq, Nk, d, args.splits)
+    ws = torch.empty((max(need, 16),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.decode_fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, num_splits=args.splits, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    esz = 2
+    algo_bytes = B * H * (2 * Nk * d * esz + 2 * Nq * d * esz + 4 * Nq)     # K, V, Q, O, lse
+    gbs = algo_bytes / (kms.mean() * 1e-3) / 1e9
+    print(f"[bench] decode {args.steps} steps: kernel mean {kms.mean() * 1e3:.1f} us, {gbs:.0f} GB/s", file=sys.stderr)
+    check = cpu = None
+    if not args.no_cpu:
+        import oracle
+        t = time.perf_counter()
+        ro, rl = oracle.attn_kv(qq.q64, kv.k64, kv.v64, scale, causal)
+        dt = time.perf_counter() - t
+        o_host = out.to(torch.float64).cpu().numpy()
+        err = np.abs(o_host - ro)
+        check = {"rows": int(B * H * Nq), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+                 "std_abs": float(err.std()), "output": args.dtype}
+        flops = 4.0 * B * H * Nq * Nk * d
+        cpu = {"value": algo_bytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"all {B * H * Nq} rows (fp64 plain definition, {dt:.2f} s, {flops / dt / 1e9:.1f} GFLOP/s)"}
+    line = {
+        "metric": "decode attention HBM GB/s (K and V read once)", "value": gbs, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"decode B{B} H{H} Nq{Nq} Nk{Nk} d{d} {args.dtype}", "B": B, "H": H, "Nq": Nq,
+                   "Nk": Nk, "d": d, "causal": causal, "num_splits": args.splits, "workspace_bytes": int(need)},
+        "check_vs_fp64_oracle": check,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
+                     "traffic": None, "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean())},
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
 
 

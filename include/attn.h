@@ -142,6 +142,35 @@ int attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* 
 /* Workspace bytes attn_naive_fwd needs: B*H*N*N elements of the input type. */
 size_t attn_naive_workspace_bytes(int B, int H, int N, int dtype);
 
+/* Key/value-cache decoding: Nq query rows against Nk cached keys (the
+ * tutorial distinguishes processing a long prompt from step-by-step generation
+ * with a key/value cache; the shapes, reuse and bottleneck differ).
+ *   q, o: DEVICE [B][H][Nq][d]; k, v: DEVICE [B][H][Nk][d]; lse [B][H][Nq] or
+ *   NULL; key_padding_mask [B][Nk] bytes or NULL.  With Nk = 0 (empty cache)
+ *   k and v may be NULL and every row gives O = 0, lse = -inf.  16-bit dtypes only
+ *   (ATTN_F16, ATTN_BF16 and their *_OUT_F32 flavours); d in {64, 128}.
+ *   causal: row i sits at position Nk - Nq + i of the sequence and sees keys
+ *   j <= Nk - Nq + i (the end of the cache); rows that see no key give O = 0
+ *   and lse = -inf, as in attn_fwd.
+ * The keys of every (b, h) are split into chunks handled independently; each
+ * chunk's partial result (acc / l, lse) goes to the workspace and a second
+ * kernel merges them: lse = log sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
+ *   num_splits: key chunks per (b, h), 0 = chosen by the library, at most 1024.
+ *   workspace: DEVICE, 16-byte aligned, at least attn_decode_workspace_bytes()
+ *   bytes, owned by the caller, not overlapping any other argument; its
+ *   contents on return are unspecified.  Two calls may not share a workspace
+ *   concurrently.
+ * Errors and stream semantics as attn_fwd; a too small or missing workspace
+ * returns ATTN_ERR_WORKSPACE, a bad num_splits ATTN_ERR_TILE. */
+int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, int dtype, void* stream,
+                    void* workspace, size_t workspace_bytes, int num_splits);
+
+/* Workspace bytes attn_decode_fwd needs for these sizes and num_splits
+ * (0 for invalid sizes). */
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
 /* Static description of a status code. */
 const char* attn_status_string(int status);
 

@@ -34,10 +34,11 @@ def _load():
         lib.oracle_attn_blocked_kvouter_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, D, I, _U8, L, I]
         lib.oracle_row_softmax_f64.argtypes = [_D, _D, L, L, _D, _D]
         lib.oracle_row_blocked_f64.argtypes = [_D, _D, _U8, L, L, L, I, I, _D, _D]
+        lib.oracle_attn_kv_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, L, D, I, _U8]
         lib.oracle_num_threads.argtypes = []
         for f in (lib.oracle_attn_f64, lib.oracle_attn_rows_f64, lib.oracle_attn_blocked_f64,
                   lib.oracle_attn_blocked_kvouter_f64, lib.oracle_row_softmax_f64,
-                  lib.oracle_row_blocked_f64, lib.oracle_num_threads):
+                  lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -142,6 +143,25 @@ def row_blocked(scores, values, width, order=0, visible=None, rescale=True):
     _check(_load().oracle_row_blocked_f64(sp, vp, vis_p, n, dv, int(width), int(order), int(bool(rescale)),
                                           out.ctypes.data_as(_D), lse.ctypes.data_as(_D)))
     return out, float(lse[0])
+
+
+def attn_kv(q, k, v, scale, causal=False, mask=None):
+    """Query block q [B,H,Nq,d] against keys/values [B,H,Nk,d], plain definition;
+    causal visibility aligned to the end of the keys (row i sees j <= Nk - Nq + i,
+    so with Nq > Nk the first Nq - Nk rows see nothing) -> (o, lse)."""
+    q, qp = _f64(q)
+    k, kp = _f64(k)
+    v, vp = _f64(v)
+    if q.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B,H,Nq,d] and k, v [B,H,Nk,d] do not match")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    mk, mp = _mask(mask, B, Nk)
+    o = np.empty((B, H, Nq, d), np.float64)
+    lse = np.empty((B, H, Nq), np.float64)
+    _check(_load().oracle_attn_kv_f64(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D),
+                                      B, H, Nq, Nk, d, float(scale), int(bool(causal)), mp))
+    return o, lse
 
 
 def num_threads():

@@ -157,6 +157,57 @@ int oracle_attn_rows_f64(const double* q, const double* k, const double* v,
 }
 
 /*
+ * Query block against a longer key/value sequence, plain definition (the
+ * tutorial's remark that prompt processing and step-by-step generation with a
+ * key/value cache have different matrix shapes: here Nq query rows meet Nk
+ * cached keys).  q, o are [B][H][Nq][d], k, v are [B][H][Nk][d], lse is
+ * [B][H][Nq], mask is [B][Nk] or NULL.  Causal visibility is aligned to the
+ * end of the cache: query row i sits at position Nk - Nq + i and sees keys
+ * j <= Nk - Nq + i (with Nq = Nk this is the j <= i prefix).
+ */
+int oracle_attn_kv_f64(const double* q, const double* k, const double* v,
+                       double* o, double* lse, long B, long H, long Nq, long Nk, long d,
+                       double scale, int causal, const unsigned char* mask)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d < 0 || !o || !lse) return -1;
+    const long rows = B * H * Nq;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (long r = 0; r < rows; ++r) {
+            const long i = r % Nq, bh = r / Nq, b = bh / H;
+            const double* qi = q + r * d;
+            const double* kb = k + bh * Nk * d;
+            const double* vb = v + bh * Nk * d;
+            const long last = causal ? Nk - Nq + i : Nk - 1;    /* last visible key */
+            double m = -INFINITY;
+            int any = 0;
+            for (long j = 0; j < Nk; ++j) {
+                if (j > last || (mask && mask[b * Nk + j] != 0)) continue;
+                s[j] = score(qi, kb + j * d, d, scale);
+                if (!any || s[j] > m) m = s[j];
+                any = 1;
+            }
+            double* orow = o + r * d;
+            for (long c = 0; c < d; ++c) orow[c] = 0.0;
+            if (!any) { lse[r] = -INFINITY; continue; }
+            double l = 0.0;
+            for (long j = 0; j < Nk; ++j) {
+                if (j > last || (mask && mask[b * Nk + j] != 0)) continue;
+                const double w = exp(s[j] - m);
+                l += w;
+                for (long c = 0; c < d; ++c) orow[c] += w * vb[j * d + c];
+            }
+            for (long c = 0; c < d; ++c) orow[c] /= l;
+            lse[r] = m + log(l);
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
  * Running state of the online merge for one row: maximum m, sum of
  * exponentials l, unnormalised weighted vector a[0..d).
  */

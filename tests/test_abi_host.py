@@ -1,6 +1,7 @@
 """C ABI checks that need no GPU: the library loads, exports every symbol the
 header declares, and rejects bad arguments on the host before any launch.
 (Addresses below are fake integers; a rejected call never dereferences them.)"""
+import ctypes
 import os
 import re
 
@@ -11,6 +12,7 @@ import tiled_online_softmax_fwd_amd as A
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 OK, NULL, SHAPE, HEAD, DTYPE, ALIGN, TILE, SCALE, ALIAS = 0, 1, 2, 3, 4, 5, 6, 7, 8
+WORKSPACE = 10
 
 
 def declared_functions():
@@ -102,3 +104,30 @@ def test_no_cpu_fallback_exists():
     src = open(os.path.join(ROOT, "tiled_online_softmax_fwd_amd", "__init__.py")).read()
     for banned in (r"softmax\(", r"matmul", r"\boracle\b", r"einsum", r"import numpy", r"\bexp\(", r"\bbmm\("):
         assert not re.search(banned, src), banned
+
+
+def test_decode_argument_checks():
+    L = A.lib()
+    q, k, v, o = (ctypes.c_void_p(x) for x in (0x10000, 0x20000, 0x30000, 0x40000))
+    ws = ctypes.c_void_p(0x100000)
+    need = L.attn_decode_workspace_bytes(1, 2, 3, 100, 64, 0)
+    assert need > 0 and L.attn_decode_workspace_bytes(1, 2, 3, 100, 96, 0) == 0
+
+    def dec(q=q, k=k, v=v, o=o, lse=None, B=1, H=2, Nq=3, Nk=100, d=64, scale=0.1, dtype=A.BF16, ws=ws,
+            nws=None, splits=0):
+        return L.attn_decode_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, 0, None, dtype, None, ws,
+                                 need if nws is None else nws, splits)
+    # rejected before anything is launched (no GPU touched)
+    assert dec(dtype=A.F32) == DTYPE
+    assert dec(d=96) == HEAD
+    assert dec(scale=0.0) == SCALE
+    assert dec(Nq=-1) == SHAPE
+    assert dec(splits=1025) == TILE
+    assert dec(q=None) == NULL
+    assert dec(k=None) == NULL
+    assert dec(q=ctypes.c_void_p(0x10008)) == ALIGN
+    assert dec(ws=None) == WORKSPACE
+    assert dec(nws=need - 4) == WORKSPACE
+    assert dec(ws=ctypes.c_void_p(0x20000 + 64)) == ALIAS    # inside k
+    assert dec(o=ctypes.c_void_p(0x10000)) == ALIAS          # o == q
+    assert dec(Nq=0, q=None, o=None) == OK                                          # empty: no-op

@@ -373,3 +373,62 @@ def test_bad_arguments_are_rejected():
         oracle.row_blocked([1.0], [[1.0]], 0)
     with pytest.raises(ValueError):
         oracle.attn_rows(np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2, 2)), 1.0, [4])
+
+
+# ------------------------------------------------- query block against a key cache
+def brute_attention_kv(q, k, v, scale, causal=False, mask=None):
+    """Independent pure-Python attention of Nq query rows against Nk keys, the
+    causal prefix aligned to the end of the keys (row i sees j <= Nk - Nq + i)."""
+    B, H, Nq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Nk = len(k[0][0])
+    O, LSE = [], []
+    for b in range(B):
+        for h in range(H):
+            for i in range(Nq):
+                cols = [j for j in range(Nk) if (not causal or j <= Nk - Nq + i) and (mask is None or mask[b][j] == 0)]
+                if not cols:
+                    O.append([0.0] * d); LSE.append(-math.inf)
+                    continue
+                s = {j: scale * math.fsum(q[b][h][i][c] * k[b][h][j][c] for c in range(d)) for j in cols}
+                top = max(s.values())
+                w = {j: math.exp(s[j] - top) for j in cols}
+                tot = math.fsum(w.values())
+                O.append([math.fsum(w[j] * v[b][h][j][c] for j in cols) / tot for c in range(d)])
+                LSE.append(top + math.log(tot))
+    return np.array(O).reshape(B, H, Nq, d), np.array(LSE).reshape(B, H, Nq)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("use_mask", [False, True])
+def test_key_cache_oracle_matches_brute_force(causal, use_mask):
+    """[P3] prompt vs cache-decoding shapes: Nq != Nk on small integer inputs,
+    against independent stdlib Python."""
+    for seed, (B, H, Nq, Nk, d) in enumerate([(1, 1, 1, 1, 1), (2, 2, 1, 9, 3), (1, 3, 4, 11, 4), (2, 1, 6, 6, 2)]):
+        rng = np.random.default_rng([40, seed])
+        q = rng.integers(-3, 4, (B, H, Nq, d)).astype(np.float64)
+        k = rng.integers(-3, 4, (B, H, Nk, d)).astype(np.float64)
+        v = rng.integers(-5, 6, (B, H, Nk, d)).astype(np.float64)
+        mask = None
+        if use_mask:
+            mask = (rng.random((B, Nk)) < 0.3).astype(np.uint8)
+            mask[0, :] = 1 if Nk == 1 else mask[0, :]
+        o, lse = oracle.attn_kv(q, k, v, 0.5, causal, mask)
+        bo, bl = brute_attention_kv(q.tolist(), k.tolist(), v.tolist(), 0.5, causal,
+                                    None if mask is None else mask.tolist())
+        np.testing.assert_allclose(o, bo, rtol=1e-13, atol=1e-13)
+        assert np.array_equal(np.isinf(lse), np.isinf(bl))
+        np.testing.assert_allclose(lse[np.isfinite(bl)], bl[np.isfinite(bl)], rtol=1e-14, atol=1e-13)
+
+
+def test_cache_decoding_equals_the_tail_of_causal_self_attention():
+    """Causal self-attention over a whole sequence and the last Nq rows decoded
+    against the full key cache are the same rows ([P3] causal prefix)."""
+    rng = np.random.default_rng([41, 0])
+    q = rng.standard_normal((2, 2, 40, 8))
+    k = rng.standard_normal((2, 2, 40, 8))
+    v = rng.standard_normal((2, 2, 40, 8))
+    o, lse = oracle.attn(q, k, v, 0.4, True)
+    for nq in (1, 3, 40):
+        od, ld = oracle.attn_kv(q[:, :, -nq:], k, v, 0.4, True)
+        np.testing.assert_allclose(od, o[:, :, -nq:], rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(ld, lse[:, :, -nq:], rtol=1e-14, atol=1e-14)

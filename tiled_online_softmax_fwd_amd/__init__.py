@@ -17,7 +17,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HE
           4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_TILE", 7: "ATTN_ERR_SCALE",
           8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
-           "attn_naive_workspace_bytes", "attn_status_string", "attn_last_error", "attn_version")
+           "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes",
+           "attn_status_string", "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -51,13 +52,16 @@ def lib():
         L.attn_naive_fwd.argtypes = common + [vp, vp, ctypes.c_size_t]
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_naive_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t, i]
+        L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
         for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_check_args, L.attn_default_tiles,
-                   L.attn_naive_fwd, L.attn_version):
+                   L.attn_naive_fwd, L.attn_decode_fwd, L.attn_version):
             fn.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,6 +156,44 @@ def naive_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=N
     st = lib().attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                               int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s),
                               _ptr(workspace), workspace.numel())
+    _raise(st)
+    return out, lse
+
+
+def decode_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=None, lse=None,
+               out_fp32=False, num_splits=0, workspace=None, want_lse=True, stream=None):
+    """Query block q [B,H,Nq,d] against a key/value cache k, v [B,H,Nk,d] through
+    attn_decode_fwd (16-bit inputs).  Returns (out, lse)."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B,H,Nq,d] and k, v [B,H,Nk,d] do not match")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous GPU tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    code = _dtype_code(q, out_fp32)
+    odt = torch.float32 if (out_fp32 or q.dtype == torch.float32) else q.dtype
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    mask = key_padding_mask
+    if mask is not None:
+        if mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (B, Nk):
+            raise ValueError("key_padding_mask must be a [B, Nk] uint8/bool tensor")
+        mask = mask.contiguous()
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    need = lib().attn_decode_workspace_bytes(B, H, Nq, Nk, d, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().attn_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                               int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s), _ptr(workspace),
+                               workspace.numel(), int(num_splits))
     _raise(st)
     return out, lse
 

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "attn.h"
+#include "decode.h"
 #include "fwd_kernel.h"
 #include "naive_kernel.h"
 
@@ -136,6 +137,31 @@ int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
     return check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
 }
 
+// Key chunks of the decode path: about two one-wave workgroups per compute
+// unit (512 in all; measured on B8 H32 Nk 8192 and B1 H32 Nk 65536, longer
+// chunks stream better than more of them), whole 32-key tiles per chunk.
+void decode_splits(int B, int H, int Nq, int Nk, int num_splits, int* splits, int* kps)
+{
+    const int tiles = (Nk + 31) / 32;
+    int s = num_splits;
+    if (s <= 0) {
+        const int64_t units = (int64_t)B * H * ((Nq + 15) / 16);
+        const int64_t want = units > 0 ? (512 + units - 1) / units : 1;
+        s = (int)(want < 1024 ? want : 1024);
+    }
+    if (s > tiles) s = tiles;
+    if (s < 1) s = 1;
+    const int per = (tiles + s - 1) / s;
+    *kps = (per > 0 ? per : 1) * 32;
+    *splits = Nk > 0 ? (Nk + *kps - 1) / *kps : 1;
+}
+
+size_t decode_ws_bytes(int B, int H, int Nq, int d, int splits)
+{
+    const size_t parts = (size_t)B * H * (size_t)splits * (size_t)Nq;
+    return parts * (size_t)d * 4 + parts * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +251,69 @@ int attn_naive_fwd(const void* q, const void* k, const void* v, void* o, float* 
     p.out_f32 = elem_bytes_out(dtype) == 4 ? 1 : 0;
     const hipError_t e = attnk::naive_launch(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "naive launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits)
+{
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk < 0 || (d != 64 && d != 128) || num_splits < 0 || num_splits > 1024) return 0;
+    int splits, kps;
+    decode_splits(B, H, Nq, Nk, num_splits, &splits, &kps);
+    return decode_ws_bytes(B, H, Nq, d, splits);
+}
+
+int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, int dtype, void* stream,
+                    void* workspace, size_t workspace_bytes, int num_splits)
+{
+    if (dtype < ATTN_F32 || dtype > ATTN_BF16_OUT_F32) return fail(ATTN_ERR_DTYPE, "dtype %d is not an attn_dtype", dtype);
+    if (dtype == ATTN_F32) return fail(ATTN_ERR_DTYPE, "the decode path takes 16-bit q, k, v");
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return fail(ATTN_ERR_SHAPE, "negative size B=%d H=%d Nq=%d Nk=%d", B, H, Nq, Nk);
+    const int64_t nmax = Nq > Nk ? Nq : Nk;
+    if ((int64_t)B * H * nmax >= ((int64_t)1 << 31)) return fail(ATTN_ERR_SHAPE, "B*H*max(Nq, Nk) exceeds 2^31 - 1");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_HEAD_DIM, "head size d=%d, supported: 64, 128", d);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_SCALE, "scale %g must be finite and > 0", (double)scale);
+    if (num_splits < 0 || num_splits > 1024) return fail(ATTN_ERR_TILE, "num_splits=%d not in 0..1024", num_splits);
+    if ((int64_t)B * H * Nq == 0) return ok();
+    if (!q || !o) return fail(ATTN_ERR_NULL, "q and o must be non-NULL");
+    if (Nk > 0 && (!k || !v)) return fail(ATTN_ERR_NULL, "k and v must be non-NULL when Nk > 0");
+    const void* p16[4] = {q, k, v, o};
+    const char* names[4] = {"q", "k", "v", "o"};
+    for (int i = 0; i < 4; ++i)
+        if ((uintptr_t)p16[i] % 16) return fail(ATTN_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    if (lse && ((uintptr_t)lse % 4)) return fail(ATTN_ERR_ALIGN, "lse is not 4-byte aligned");
+    const size_t nq = (size_t)B * H * Nq * d * elem_bytes_in(dtype), nkv = (size_t)B * H * Nk * d * elem_bytes_in(dtype);
+    const size_t no = (size_t)B * H * Nq * d * elem_bytes_out(dtype), nl = lse ? (size_t)B * H * Nq * 4 : 0;
+    if (overlaps(o, no, q, nq) || overlaps(o, no, k, nkv) || overlaps(o, no, v, nkv) || overlaps(o, no, lse, nl))
+        return fail(ATTN_ERR_ALIAS, "o overlaps q, k, v or lse");
+    if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv))
+        return fail(ATTN_ERR_ALIAS, "lse overlaps q, k or v");
+    int splits, kps;
+    decode_splits(B, H, Nq, Nk, num_splits, &splits, &kps);
+    if ((int64_t)B * H * splits >= ((int64_t)1 << 31) || (Nq + 15) / 16 > 65535)
+        return fail(ATTN_ERR_SHAPE, "decode grid too large (B*H*splits = %lld, Nq = %d)", (long long)B * H * splits, Nq);
+    const size_t need = decode_ws_bytes(B, H, Nq, d, splits);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16))
+        return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned", need);
+    if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nkv) || overlaps(workspace, need, v, nkv) ||
+        overlaps(workspace, need, o, no) || overlaps(workspace, need, lse, nl))
+        return fail(ATTN_ERR_ALIAS, "workspace overlaps an input or output");
+
+    attnk::DecParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)workspace + (size_t)B * H * splits * (size_t)Nq * d;
+    p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
+    p.splits = splits; p.keys_per_split = kps;
+    p.scale = scale;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.slack = 0.f;
+    p.causal = causal ? 1 : 0;
+    p.out_f32 = elem_bytes_out(dtype) == 4 ? 1 : 0;
+    const int bits = (dtype == ATTN_BF16 || dtype == ATTN_BF16_OUT_F32) ? 0 : 1;
+    const hipError_t e = attnk::lookup_decode(bits, d)(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ok();
 }
 
