@@ -78,8 +78,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
     ap.add_argument("--naive", action="store_true", help="also time the materialising baseline")
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode"],
-                    help="prefill: the causal forward (default); decode: Nq query rows against a key/value cache")
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "backward"],
+                    help="prefill: the causal forward (default); decode: Nq query rows against a key/value "
+                         "cache; backward: gradient of the forward")
     ap.add_argument("--Nq", type=int, default=1, help="decode: query rows per head")
     ap.add_argument("--Nk", type=int, default=8192, help="decode: cached keys per head")
     ap.add_argument("--decode-B", type=int, default=8, help="decode: batch")
@@ -115,6 +116,8 @@ def main():
 
     if args.workload == "decode":
         return run_decode(args, torch, synth, A)
+    if args.workload == "backward":
+        return run_backward(args, torch, synth, A)
 
     B, H, N, d = args.B, args.H, args.N, args.d
     causal = not args.no_causal
@@ -242,6 +245,70 @@ def main():
     }
     if naive:
         line["naive_baseline"] = naive
+    print(json.dumps(line), flush=True)
+
+
+def run_backward(args, torch, synth, A):
+    """Gradient of the forward on the prefill shape; algorithmic work is the five
+    products S, dP, dV, dK, dQ (2.5x the forward's FLOPs, halved for causal)."""
+    B, H, N, d = args.B, args.H, args.N, args.d
+    if args.dtype == "f32":
+        print("the backward takes 16-bit inputs", file=sys.stderr)
+        sys.exit(2)
+    causal = not args.no_causal
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    print(f"[bench] backward inputs B{B} H{H} N{N} d{d} {args.dtype}", file=sys.stderr, flush=True)
+    p = synth.make_qkv(B, H, N, d, args.dtype, 5)
+    g = synth.make_qkv(B, H, N, d, args.dtype, 5, variant=1)
+    q, k, v = synth.upload(p)
+    dout = synth.to_torch(g.q, args.dtype)
+    o, lse = A.fwd(q, k, v, scale=scale, causal=causal)
+    ws = torch.empty((max(A.lib().attn_bwd_workspace_bytes(B, H, N), 16),), dtype=torch.uint8, device="cuda")
+    res = {}
+
+    def step():
+        res["g"] = A.bwd(q, k, v, o, dout, lse, scale=scale, causal=causal, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    fl = 2.5 * flops(B, H, N, d, causal)
+    tf = fl / (kms.mean() * 1e-3) / 1e12
+    print(f"[bench] backward {args.steps} steps: mean {kms.mean():.3f} ms, {tf:.0f} TFLOP/s", file=sys.stderr)
+    check = None
+    if not args.no_cpu:
+        import oracle
+        heads = min(H, 2)
+        t = time.perf_counter()
+        rq, rk, rv = oracle.attn_bwd(p.q64[:, :heads], p.k64[:, :heads], p.v64[:, :heads], g.q64[:, :heads],
+                                     scale, causal)
+        dt = time.perf_counter() - t
+        check = {"heads_checked": heads, "time_s": dt}
+        for name, x, r in zip(("dq", "dk", "dv"), res["g"], (rq, rk, rv)):
+            e = np.abs(x[:, :heads].to(torch.float64).cpu().numpy() - r)
+            check[name] = {"max_abs": float(e.max()), "mean_abs": float(e.mean()), "max_ref": float(np.abs(r).max())}
+    line = {
+        "metric": "attention backward TFLOP/s (5 products, halved for causal)", "value": fl / (wall / args.steps) / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"backward B{B} H{H} N{N} d{d} {args.dtype} {'causal' if causal else 'non-causal'}",
+                   "B": B, "H": H, "N": N, "d": d, "causal": causal},
+        "check_vs_fp64_oracle": check,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "bwd_pre + bwd_dkdv + bwd_dq",
+                     "kernel_ms_mean": float(kms.mean())},
+    }
     print(json.dumps(line), flush=True)
 
 

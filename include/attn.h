@@ -171,6 +171,25 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
  * (0 for invalid sizes). */
 size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 
+/* Gradient of attn_fwd w.r.t. q, k and v (the tutorial asks to check outputs
+ * and gradients).  Recomputes P tile by tile from the forward's lse:
+ * P_ij = exp(scale q_i.k_j - lse_i), D_i = sum_c dout_ic o_ic,
+ * dv = P^T dout, ds = P (dout v^T - D), dq = scale ds k, dk = scale ds^T q.
+ *   q, k, v, o, dout: DEVICE [B][H][N][d] in the input type, 16-byte aligned
+ *   (o and lse as written by attn_fwd with the same arguments).
+ *   lse: DEVICE [B][H][N] float.  dq, dk, dv: DEVICE [B][H][N][d] float,
+ *   16-byte aligned, not overlapping anything else.
+ *   dtype: ATTN_BF16 or ATTN_F16.  Masking as attn_fwd; rows with no visible
+ *   key contribute nothing.
+ *   workspace: DEVICE, 16-byte aligned, attn_bwd_workspace_bytes() bytes.
+ * Deterministic (no atomics).  Errors and stream semantics as attn_fwd. */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* key_padding_mask, int dtype, void* stream, void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes attn_bwd needs (8 per row). */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
 /* Static description of a status code. */
 const char* attn_status_string(int status);
 

@@ -35,10 +35,11 @@ def _load():
         lib.oracle_row_softmax_f64.argtypes = [_D, _D, L, L, _D, _D]
         lib.oracle_row_blocked_f64.argtypes = [_D, _D, _U8, L, L, L, I, I, _D, _D]
         lib.oracle_attn_kv_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, L, D, I, _U8]
+        lib.oracle_attn_bwd_f64.argtypes = [_D, _D, _D, _D, _D, _D, _D, L, L, L, L, D, I, _U8]
         lib.oracle_num_threads.argtypes = []
         for f in (lib.oracle_attn_f64, lib.oracle_attn_rows_f64, lib.oracle_attn_blocked_f64,
                   lib.oracle_attn_blocked_kvouter_f64, lib.oracle_row_softmax_f64,
-                  lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64):
+                  lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64, lib.oracle_attn_bwd_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -162,6 +163,23 @@ def attn_kv(q, k, v, scale, causal=False, mask=None):
     _check(_load().oracle_attn_kv_f64(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D),
                                       B, H, Nq, Nk, d, float(scale), int(bool(causal)), mp))
     return o, lse
+
+
+def attn_bwd(q, k, v, dout, scale, causal=False, mask=None):
+    """Gradient of the plain definition w.r.t. q, k, v for the output cotangent
+    dout (all [B,H,N,d], fp64) -> (dq, dk, dv)."""
+    keep, (qp, kp, vp) = _qkv(q, k, v)
+    g, gp = _f64(dout)
+    if g.shape != keep[0].shape:
+        raise ValueError("dout must match q")
+    B, H, N, d = keep[0].shape
+    mk, mp = _mask(mask, B, N)
+    dq = np.empty((B, H, N, d), np.float64)
+    dk = np.empty((B, H, N, d), np.float64)
+    dv = np.empty((B, H, N, d), np.float64)
+    _check(_load().oracle_attn_bwd_f64(qp, kp, vp, gp, dq.ctypes.data_as(_D), dk.ctypes.data_as(_D),
+                                       dv.ctypes.data_as(_D), B, H, N, d, float(scale), int(bool(causal)), mp))
+    return dq, dk, dv
 
 
 def num_threads():

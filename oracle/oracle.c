@@ -157,6 +157,75 @@ int oracle_attn_rows_f64(const double* q, const double* k, const double* v,
 }
 
 /*
+ * Gradient of the plain definition (reverse mode of softmax(scale q k^T) v),
+ * written out from the definition with the chain rule: for one (b, h), with
+ * P the row softmax over visible keys and O = P V,
+ *     dV = P^T dO,   dP = dO V^T,   dS_ij = P_ij (dP_ij - sum_c dO_ic O_ic),
+ *     dQ = scale dS K,   dK = scale dS^T Q.
+ * Masked pairs have P = 0 and contribute nothing; a row with no visible key
+ * has O = 0 and contributes nothing.  All [B][H][N][d]; fp64 throughout.
+ */
+int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dout,
+                        double* dq, double* dk, double* dv, long B, long H, long N, long d,
+                        double scale, int causal, const unsigned char* mask)
+{
+    if (bad_sizes(B, H, N, d) || !dq || !dk || !dv) return -1;
+    const long BH = B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < BH; ++bh) {
+        const long b = bh / H;
+        const double* Q = q + bh * N * d;
+        const double* K = k + bh * N * d;
+        const double* V = v + bh * N * d;
+        const double* dO = dout + bh * N * d;
+        double* dQ = dq + bh * N * d;
+        double* dK = dk + bh * N * d;
+        double* dV = dv + bh * N * d;
+        for (long t = 0; t < N * d; ++t) { dQ[t] = 0.0; dK[t] = 0.0; dV[t] = 0.0; }
+        double* P = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* orow = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        for (long i = 0; i < N; ++i) {
+            /* forward for row i: P_i. and O_i */
+            double m = -INFINITY;
+            int any = 0;
+            for (long j = 0; j < N; ++j) {
+                if (!visible(b, i, j, N, causal, mask)) { P[j] = -INFINITY; continue; }
+                P[j] = score(Q + i * d, K + j * d, d, scale);
+                if (!any || P[j] > m) m = P[j];
+                any = 1;
+            }
+            if (!any) continue;
+            double l = 0.0;
+            for (long j = 0; j < N; ++j) {
+                P[j] = (P[j] == -INFINITY) ? 0.0 : exp(P[j] - m);
+                l += P[j];
+            }
+            for (long c = 0; c < d; ++c) orow[c] = 0.0;
+            for (long j = 0; j < N; ++j) {
+                P[j] /= l;
+                for (long c = 0; c < d; ++c) orow[c] += P[j] * V[j * d + c];
+            }
+            double Di = 0.0;                       /* sum_c dO_ic O_ic */
+            for (long c = 0; c < d; ++c) Di += dO[i * d + c] * orow[c];
+            for (long j = 0; j < N; ++j) {
+                if (P[j] == 0.0) continue;
+                double dPij = 0.0;
+                for (long c = 0; c < d; ++c) dPij += dO[i * d + c] * V[j * d + c];
+                const double dSij = P[j] * (dPij - Di);
+                for (long c = 0; c < d; ++c) {
+                    dV[j * d + c] += P[j] * dO[i * d + c];
+                    dQ[i * d + c] += scale * dSij * K[j * d + c];
+                    dK[j * d + c] += scale * dSij * Q[i * d + c];
+                }
+            }
+        }
+        free(P);
+        free(orow);
+    }
+    return 0;
+}
+
+/*
  * Query block against a longer key/value sequence, plain definition (the
  * tutorial's remark that prompt processing and step-by-step generation with a
  * key/value cache have different matrix shapes: here Nq query rows meet Nk

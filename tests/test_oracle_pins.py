@@ -432,3 +432,42 @@ def test_cache_decoding_equals_the_tail_of_causal_self_attention():
         od, ld = oracle.attn_kv(q[:, :, -nq:], k, v, 0.4, True)
         np.testing.assert_allclose(od, o[:, :, -nq:], rtol=1e-14, atol=1e-14)
         np.testing.assert_allclose(ld, lse[:, :, -nq:], rtol=1e-14, atol=1e-14)
+
+
+# --------------------------------------------------------------- gradient
+def test_gradient_matches_central_differences():
+    """dL/dq, dL/dk, dL/dv of L = sum(dO * O) against central differences of the
+    oracle's own forward (fp64, step 1e-6): independent of the gradient formula."""
+    rng = np.random.default_rng([42, 0])
+    for causal, use_mask in ((False, False), (True, False), (False, True)):
+        B, H, N, d = 1, 2, 6, 3
+        q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+        mask = None
+        if use_mask:
+            mask = np.zeros((B, N), np.uint8); mask[0, [1, 4]] = 1
+        dq, dk, dv = oracle.attn_bwd(q, k, v, g, 0.6, causal, mask)
+        h = 1e-6
+        for x, dx in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                op, _ = oracle.attn(q, k, v, 0.6, causal, mask)
+                x[idx] = old - h
+                om, _ = oracle.attn(q, k, v, 0.6, causal, mask)
+                x[idx] = old
+                num[idx] = np.sum(g * (op - om)) / (2 * h)
+            np.testing.assert_allclose(dx, num, rtol=1e-6, atol=1e-8)
+
+
+def test_gradient_sum_rules():
+    """Rows of P sum to one and rows of dS to zero, so sum_j dV_j = sum_i dO_i
+    and (non-causal, unmasked) sum_j dK_j = 0; a fully masked row contributes nothing."""
+    rng = np.random.default_rng([43, 0])
+    q, k, v, g = (rng.standard_normal((2, 2, 17, 5)) for _ in range(4))
+    dq, dk, dv = oracle.attn_bwd(q, k, v, g, 0.4)
+    np.testing.assert_allclose(dv.sum(axis=2), g.sum(axis=2), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    mask = np.zeros((2, 17), np.uint8); mask[1, :] = 1
+    dq, dk, dv = oracle.attn_bwd(q, k, v, g, 0.4, False, mask)
+    assert np.all(dq[1] == 0) and np.all(dk[1] == 0) and np.all(dv[1] == 0)

@@ -18,6 +18,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HE
           8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
            "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes",
+           "attn_bwd", "attn_bwd_workspace_bytes",
            "attn_status_string", "attn_last_error", "attn_version")
 
 
@@ -55,13 +56,16 @@ def lib():
         L.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t, i]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t]
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
         for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_check_args, L.attn_default_tiles,
-                   L.attn_naive_fwd, L.attn_decode_fwd, L.attn_version):
+                   L.attn_naive_fwd, L.attn_decode_fwd, L.attn_bwd, L.attn_version):
             fn.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,6 +200,38 @@ def decode_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=
                                workspace.numel(), int(num_splits))
     _raise(st)
     return out, lse
+
+
+def bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, key_padding_mask=None, workspace=None, stream=None):
+    """Gradient of fwd w.r.t. q, k, v through attn_bwd (bf16 or f16 inputs; o and
+    lse as returned by fwd with the same arguments).  Returns fp32 (dq, dk, dv)."""
+    torch = _torch()
+    for t in (q, k, v, o, dout):
+        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("the backward takes bf16 or fp16 tensors")
+    B, H, N, d = q.shape
+    code = BF16 if q.dtype == torch.bfloat16 else F16
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    mask = key_padding_mask
+    if mask is not None:
+        if mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (B, N):
+            raise ValueError("key_padding_mask must be a [B, N] uint8/bool tensor")
+        mask = mask.contiguous()
+    need = lib().attn_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, H, N, d, float(scale), int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s),
+                        _ptr(workspace), workspace.numel())
+    _raise(st)
+    return dq, dk, dv
 
 
 def check_args(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale, causal, mask_ptr, dtype,

@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "attn.h"
+#include "bwd.h"
 #include "decode.h"
 #include "fwd_kernel.h"
 #include "naive_kernel.h"
@@ -314,6 +315,67 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
     const int bits = (dtype == ATTN_BF16 || dtype == ATTN_BF16_OUT_F32) ? 0 : 1;
     const hipError_t e = attnk::lookup_decode(bits, d)(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N)
+{
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    return (size_t)B * H * (size_t)N * 8;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* key_padding_mask, int dtype, void* stream, void* workspace, size_t workspace_bytes)
+{
+    if (dtype < ATTN_F32 || dtype > ATTN_BF16_OUT_F32) return fail(ATTN_ERR_DTYPE, "dtype %d is not an attn_dtype", dtype);
+    if (dtype != ATTN_BF16 && dtype != ATTN_F16) return fail(ATTN_ERR_DTYPE, "the backward takes ATTN_BF16 or ATTN_F16");
+    int st = check_scalars(B, H, N, d, scale, dtype);
+    if (st) return st;
+    if ((int64_t)B * H * N == 0) return ok();
+    const void* in[5] = {q, k, v, o, dout};
+    const char* nin[5] = {"q", "k", "v", "o", "dout"};
+    void* out[3] = {dq, dk, dv};
+    const char* nout[3] = {"dq", "dk", "dv"};
+    for (int i = 0; i < 5; ++i) {
+        if (!in[i]) return fail(ATTN_ERR_NULL, "%s must be non-NULL", nin[i]);
+        if ((uintptr_t)in[i] % 16) return fail(ATTN_ERR_ALIGN, "%s is not 16-byte aligned", nin[i]);
+    }
+    for (int i = 0; i < 3; ++i) {
+        if (!out[i]) return fail(ATTN_ERR_NULL, "%s must be non-NULL", nout[i]);
+        if ((uintptr_t)out[i] % 16) return fail(ATTN_ERR_ALIGN, "%s is not 16-byte aligned", nout[i]);
+    }
+    if (!lse) return fail(ATTN_ERR_NULL, "lse must be non-NULL");
+    if ((uintptr_t)lse % 4) return fail(ATTN_ERR_ALIGN, "lse is not 4-byte aligned");
+    const size_t rows = (size_t)B * H * N;
+    const size_t nt = rows * d * 2, nf = rows * d * 4, nl = rows * 4;
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(out[i], nf, in[j], nt)) return fail(ATTN_ERR_ALIAS, "%s overlaps %s", nout[i], nin[j]);
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], nf, out[j], nf)) return fail(ATTN_ERR_ALIAS, "%s overlaps %s", nout[i], nout[j]);
+        if (overlaps(out[i], nf, lse, nl)) return fail(ATTN_ERR_ALIAS, "%s overlaps lse", nout[i]);
+    }
+    const size_t need = attn_bwd_workspace_bytes(B, H, N);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % 16))
+        return fail(ATTN_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned", need);
+    for (int j = 0; j < 5; ++j)
+        if (overlaps(workspace, need, in[j], nt)) return fail(ATTN_ERR_ALIAS, "workspace overlaps %s", nin[j]);
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, need, out[i], nf)) return fail(ATTN_ERR_ALIAS, "workspace overlaps %s", nout[i]);
+    if (overlaps(workspace, need, lse, nl)) return fail(ATTN_ERR_ALIAS, "workspace overlaps lse");
+
+    attnk::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.mask = key_padding_mask;
+    p.dsum = (float*)workspace;
+    p.lse2 = (float*)workspace + rows;
+    p.B = B; p.H = H; p.N = N;
+    p.scale = scale;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.causal = causal ? 1 : 0;
+    const hipError_t e = attnk::lookup_bwd(dtype == ATTN_BF16 ? 0 : 1, d)(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();
 }
 

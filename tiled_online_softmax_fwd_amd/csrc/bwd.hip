@@ -1,0 +1,348 @@
+// bwd.hip -- gradient of the attention forward w.r.t. q, k and v.
+//
+// The tutorial's checklist asks for numerical closeness of outputs and of
+// gradients.  The gradient is recomputed tile by tile from the forward's
+// log-sum-exp, the same way the forward never stores the N x N matrix: with
+// P_ij = exp(scale q_i.k_j - lse_i) and D_i = sum_c dO_ic O_ic,
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
+//     dK = scale dS^T Q.
+// Three kernels, no atomics (bitwise deterministic):
+//   bwd_pre   D_i and lse_i * log2(e) per row (+inf for a row with no visible
+//             key, so that its P is exactly 0);
+//   bwd_dkdv  one workgroup per 32*NW keys (each wave owns 32 keys, whose K and
+//             V operands stay in registers), looping over 32-query tiles of Q
+//             and dO staged in LDS: S = Q K^T and dP = dO V^T put a key in each
+//             lane's column, which is the A-operand layout of dV += P^T dO and
+//             dK += dS^T Q (their dO and Q operands are transposing LDS reads);
+//   bwd_dq    one workgroup per 32*NW queries (Q and dO in registers), looping
+//             over 64-key tiles of K and V in LDS: S^T = K Q^T and
+//             dP^T = V dO^T put a query in each lane's column, the B-operand
+//             layout of dQ^T += K^T dS^T (K^T read transposed from LDS).
+// Products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation; P and
+// dS are rounded to the input type for the MFMA, as P is in the forward.
+#include <hip/hip_runtime.h>
+#include "bwd.h"
+#include "fwd_kernel.h"
+
+namespace attnk {
+
+// D_i and the base-2 lse of each row; one thread per row.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_pre(BwdParams p)
+{
+    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t rows = (size_t)p.B * p.H * p.N;
+    if (row >= rows) return;
+    typedef __attribute__((ext_vector_type(8))) T t8;
+    const t8* o = (const t8*)((const T*)p.o + row * D);
+    const t8* g = (const t8*)((const T*)p.dout + row * D);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+        const t8 a = o[c], b = g[c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    }
+    p.dsum[row] = acc;
+    const float l = p.lse[row];
+    p.lse2[row] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+}
+
+// Transposing LDS read of the 32x32x16 operand that holds, for lane
+// (column c = lane % 32 of the 32-column block db, half hh = lane / 32),
+// tile[rows 16*ks2 + 4*hh + 0..3 and + 8 .. + 11][32*db + c] of a row-major
+// tile stored with the swz_k chunk swizzle.
+template <int CPR>
+__device__ __forceinline__ u32x4 tr_operand(const void* tile, int ks2, int db, int lane)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __attribute__((address_space(3))) char lds_char;
+    const int hh = lane >> 5, g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
+    const int chunk = db * 4 + 2 * g + (qsrc >> 1);
+    const int row1 = ks2 * 16 + 4 * hh + rsrc, row2 = row1 + 8;
+    lds_char* base = (lds_char*)tile;
+    const int off1 = (row1 * CPR + swz_k<CPR>(row1, chunk)) * 16 + (qsrc & 1) * 8;
+    const int off2 = (row2 * CPR + swz_k<CPR>(row2, chunk)) * 16 + (qsrc & 1) * 8;
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off1));
+    const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off2));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
+    return (u32x4){w1[0], w1[1], w2[0], w2[1]};
+}
+
+// Round the 8 accumulator values of chunk ks2 (elements 8*ks2 .. 8*ks2+7) to T.
+template <typename T>
+__device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
+{
+    typename H16<T>::v8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (T)x[8 * ks2 + i];
+    return r;
+}
+
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dkdv(BwdParams p)
+{
+    using TR = H16<T>;
+    using v8 = typename TR::v8;
+    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 32;
+    using Plan = TilePlan<BQ, CPR, NW, 0>;
+    __shared__ u32x4 sq[2][BQ * CPR];
+    __shared__ u32x4 sg[2][BQ * CPR];
+    __shared__ float s_l2[2][BQ];
+    __shared__ float s_d[2][BQ];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int hh = lane >> 5, col = lane & 31;
+    const int N = p.N;
+    const int bh = blockIdx.x % (p.B * p.H);
+    const int kt = blockIdx.x / (p.B * p.H);
+    const int b = bh / p.H;
+    const size_t head = (size_t)bh * N * D;
+    const T* __restrict__ Q = (const T*)p.q + head;
+    const T* __restrict__ K = (const T*)p.k + head;
+    const T* __restrict__ V = (const T*)p.v + head;
+    const T* __restrict__ G = (const T*)p.dout + head;
+    const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
+    const float* __restrict__ DS = p.dsum + (size_t)bh * N;
+    const int k_wave = kt * 32 * NW + wave * 32;      // first key of this wave
+    const int key = k_wave + col;                     // this lane's key
+    const int krow = min(key, N - 1);
+    const bool key_on = key < N && !(p.mask && p.mask[(size_t)b * N + krow]);
+
+    // K^T and V^T operands of this lane's key: head columns 16*ks + 8*hh + 0..7
+    u32x4 kw[DK], vw[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+        kw[ks] = *(const u32x4*)(K + (size_t)krow * D + ks * 16 + hh * 8);
+        vw[ks] = *(const u32x4*)(V + (size_t)krow * D + ks * 16 + hh * 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) { asm volatile("" : "+v"(kw[ks])); asm volatile("" : "+v"(vw[ks])); }
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { dk[db] = (f32x16){}; dv[db] = (f32x16){}; }
+
+    // query tiles that can see any key of the workgroup
+    const int k_wg = kt * 32 * NW;
+    const int qt0 = p.causal ? k_wg / BQ : 0;
+    const int nqt = (N + BQ - 1) / BQ;
+    Plan plan;
+    plan.init(wave, lane);
+    const float c = p.c;
+
+    auto stage = [&](int buf, int qt) __attribute__((always_inline)) {
+        plan.issue(sq[buf], Q, qt * BQ, N, wave);
+        plan.issue(sg[buf], G, qt * BQ, N, wave);
+    };
+    if (qt0 < nqt) stage(0, qt0);
+
+    for (int qt = qt0; qt < nqt; ++qt) {
+        const int buf = (qt - qt0) & 1;
+        const int q0 = qt * BQ;
+        // tile qt landed; every wave is done with tile qt-1 (other buffer)
+        if (threadIdx.x < BQ) {
+            const int qr = min(q0 + (int)threadIdx.x, N - 1);
+            s_l2[buf][threadIdx.x] = (q0 + (int)threadIdx.x < N) ? L2[qr] : INFINITY;
+            s_d[buf][threadIdx.x] = DS[qr];
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
+
+        // S = Q K^T and dP = dO V^T: lane holds key column `col`, query rows
+        // 8*(j/4) + 4*hh + j%4 of the 32-query tile
+        f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            const u32x4 qa = sq[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
+            const u32x4 ga = sg[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
+            s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
+            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, vw[ks]), dp);
+        }
+        // P = exp2(s*c - lse2) (0 for masked pairs); dS = P (dP - D)
+        f32x16 pp, dsv;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int qr = 8 * (j >> 2) + 4 * hh + (j & 3);
+            const int qi = q0 + qr;
+            bool vis = key_on && qi < N;
+            if (p.causal) vis = vis && key <= qi;
+            const float pv = vis ? fast_exp2(fmaf(s[j], c, -s_l2[buf][qr])) : 0.f;
+            pp[j] = pv;
+            dsv[j] = pv * (dp[j] - s_d[buf][qr]);
+        }
+        // dV += P^T dO and dK += dS^T Q, contraction over the 32 queries
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const v8 pa = pack8<T>(pp, ks2), da = pack8<T>(dsv, ks2);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 gb = tr_operand<CPR>(sg[buf], ks2, db, lane);
+                const u32x4 qb = tr_operand<CPR>(sq[buf], ks2, db, lane);
+                dv[db] = TR::mma32(pa, __builtin_bit_cast(v8, gb), dv[db]);
+                dk[db] = TR::mma32(da, __builtin_bit_cast(v8, qb), dk[db]);
+            }
+        }
+    }
+
+    // dV[key][d] and dK[key][d]: accumulator block db holds head column
+    // 32*db + col and keys 8*(j/4) + 4*hh + j%4 of the wave's 32 keys
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int kr = k_wave + 8 * (j >> 2) + 4 * hh + (j & 3);
+            if (kr < N) {
+                const size_t idx = head + (size_t)kr * D + 32 * db + col;
+                p.dv[idx] = dv[db][j];
+                p.dk[idx] = dk[db][j] * sc;
+            }
+        }
+    }
+}
+
+template <typename T, int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_dq(BwdParams p)
+{
+    using TR = H16<T>;
+    using v8 = typename TR::v8;
+    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BC = 64, NKB = BC / 32, KS = BC / 16;
+    using Plan = TilePlan<BC, CPR, NW, 0>;
+    __shared__ u32x4 sk[2][BC * CPR];
+    __shared__ u32x4 sv[2][BC * CPR];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int hh = lane >> 5, col = lane & 31;
+    const int N = p.N;
+    const int bh = blockIdx.x % (p.B * p.H);
+    const int qt = blockIdx.x / (p.B * p.H);
+    const int b = bh / p.H;
+    const size_t head = (size_t)bh * N * D;
+    const T* __restrict__ Q = (const T*)p.q + head;
+    const T* __restrict__ K = (const T*)p.k + head;
+    const T* __restrict__ V = (const T*)p.v + head;
+    const T* __restrict__ G = (const T*)p.dout + head;
+    const int q0 = qt * 32 * NW;
+    const int qi = q0 + wave * 32 + col;              // this lane's query
+    const int qrow = min(qi, N - 1);
+    const float l2 = qi < N ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
+    const float dsum = p.dsum[(size_t)bh * N + qrow];
+    const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
+
+    u32x4 qw[DK], gw[DK];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+        qw[ks] = *(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8);
+        gw[ks] = *(const u32x4*)(G + (size_t)qrow * D + ks * 16 + hh * 8);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) { asm volatile("" : "+v"(qw[ks])); asm volatile("" : "+v"(gw[ks])); }
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
+
+    const int nkt = (N + BC - 1) / BC;
+    const int kt_end = p.causal ? min(nkt, (min(q0 + 32 * NW, N) - 1) / BC + 1) : nkt;
+    Plan plan;
+    plan.init(wave, lane);
+    const float c = p.c;
+    if (kt_end > 0) {
+        plan.issue(sk[0], K, 0, N, wave);
+        plan.issue(sv[0], V, 0, N, wave);
+    }
+    for (int kt = 0; kt < kt_end; ++kt) {
+        const int buf = kt & 1;
+        const int k0 = kt * BC;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + 1 < kt_end) {
+            plan.issue(sk[buf ^ 1], K, k0 + BC, N, wave);
+            plan.issue(sv[buf ^ 1], V, k0 + BC, N, wave);
+        }
+        // S^T = K Q^T and dP^T = V dO^T: lane holds query column `col`, key
+        // rows 32*kb + 8*(j/4) + 4*hh + j%4
+        f32x16 s[NKB], dp[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = (f32x16){};
+            dp[kb] = (f32x16){};
+            const int r = kb * 32 + col;
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) {
+                const u32x4 ka = sk[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                const u32x4 va = sv[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                s[kb] = TR::mma32(__builtin_bit_cast(v8, ka), __builtin_bit_cast(v8, qw[ks]), s[kb]);
+                dp[kb] = TR::mma32(__builtin_bit_cast(v8, va), __builtin_bit_cast(v8, gw[ks]), dp[kb]);
+            }
+        }
+        // dS^T = P^T (dP^T - D), P^T = exp2(s*c - lse2), 0 for masked pairs
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                bool vis = key < N && qi < N;
+                if (p.causal) vis = vis && key <= qi;
+                if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
+                const float pv = vis ? fast_exp2(fmaf(s[kb][j], c, -l2)) : 0.f;
+                s[kb][j] = pv * (dp[kb][j] - dsum);
+            }
+        }
+        // dQ^T += K^T dS^T, contraction over the tile's keys
+#pragma unroll
+        for (int ks2 = 0; ks2 < KS; ++ks2) {
+            const v8 da = pack8<T>(s[ks2 >> 1], ks2 & 1);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 ka = tr_operand<CPR>(sk[buf], ks2, db, lane);
+                dq[db] = TR::mma32(__builtin_bit_cast(v8, ka), da, dq[db]);
+            }
+        }
+    }
+
+    // dQ[query][d]: block db holds head columns 32*db + 8*(j/4) + 4*hh + j%4
+    if (qi < N) {
+        const float sc = p.scale;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = db * 32 + 8 * g4 + 4 * hh;
+                *(f32x4*)(p.dq + head + (size_t)qi * D + d0) =
+                    (f32x4){dq[db][4 * g4] * sc, dq[db][4 * g4 + 1] * sc, dq[db][4 * g4 + 2] * sc, dq[db][4 * g4 + 3] * sc};
+            }
+        }
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t st)
+{
+    constexpr int NW = 4;
+    const size_t rows = (size_t)p.B * p.H * p.N;
+    hipLaunchKernelGGL((bwd_pre<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned tiles = (unsigned)((p.N + 32 * NW - 1) / (32 * NW));
+    hipLaunchKernelGGL((bwd_dkdv<T, D, NW>), dim3((unsigned)(p.B * p.H) * tiles), dim3(NW * 64), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq<T, D, NW>), dim3((unsigned)(p.B * p.H) * tiles), dim3(NW * 64), 0, st, p);
+    return hipGetLastError();
+}
+
+BwdLaunchFn lookup_bwd(int dtype_bits, int D)
+{
+    if (dtype_bits == 0) return D == 128 ? &launch_bwd<__bf16, 128> : D == 64 ? &launch_bwd<__bf16, 64> : nullptr;
+    if (dtype_bits == 1) return D == 128 ? &launch_bwd<_Float16, 128> : D == 64 ? &launch_bwd<_Float16, 64> : nullptr;
+    return nullptr;
+}
+
+}  // namespace attnk
