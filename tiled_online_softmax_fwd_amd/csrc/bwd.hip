@@ -26,26 +26,30 @@
 
 namespace attnk {
 
-// D_i and the base-2 lse of each row; one thread per row.
+// D_i and the base-2 lse of each row.  D/8 consecutive lanes share a row and
+// read it with one 16-byte load each; the partial sums meet by xor-shuffles.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd_pre(BwdParams p)
 {
-    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+    constexpr int LPR = D / 8;                        // lanes per row
     const size_t rows = (size_t)p.B * p.H * p.N;
-    if (row >= rows) return;
+    const size_t row = (size_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
     typedef __attribute__((ext_vector_type(8))) T t8;
-    const t8* o = (const t8*)((const T*)p.o + row * D);
-    const t8* g = (const t8*)((const T*)p.dout + row * D);
     float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const t8 a = o[c], b = g[c];
+    if (row < rows) {
+        const t8 a = *((const t8*)((const T*)p.o + row * D) + part);
+        const t8 b = *((const t8*)((const T*)p.dout + row * D) + part);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
     }
-    p.dsum[row] = acc;
-    const float l = p.lse[row];
-    p.lse2[row] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+#pragma unroll
+    for (int w = LPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w);
+    if (row < rows && part == 0) {
+        p.dsum[row] = acc;
+        const float l = p.lse[row];
+        p.lse2[row] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+    }
 }
 
 // Transposing LDS read of the 32x32x16 operand that holds, for lane
@@ -80,7 +84,7 @@ __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
 }
 
 template <typename T, int D, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 bwd_dkdv(BwdParams p)
 {
     using TR = H16<T>;
@@ -206,7 +210,7 @@ bwd_dkdv(BwdParams p)
 }
 
 template <typename T, int D, int NW>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 bwd_dq(BwdParams p)
 {
     using TR = H16<T>;
@@ -325,9 +329,12 @@ bwd_dq(BwdParams p)
 template <typename T, int D>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st)
 {
-    constexpr int NW = 4;
+    // eight waves (two per SIMD) at d = 128; at d = 64 a 32-row tile has too
+    // few 16-byte chunks for eight waves' copy instructions, so four
+    constexpr int NW = D == 128 ? 8 : 4;
     const size_t rows = (size_t)p.B * p.H * p.N;
-    hipLaunchKernelGGL((bwd_pre<T, D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+    constexpr size_t RPB = 256 / (D / 8);            // rows per block of bwd_pre
+    hipLaunchKernelGGL((bwd_pre<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)((p.N + 32 * NW - 1) / (32 * NW));
