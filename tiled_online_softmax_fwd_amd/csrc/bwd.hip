@@ -14,7 +14,8 @@
 //             and dO staged in LDS: S = Q K^T and dP = dO V^T put a key in each
 //             lane's column, which is the A-operand layout of dV += P^T dO and
 //             dK += dS^T Q (their dO and Q operands are transposing LDS reads);
-//   bwd_dq    one workgroup per 32*NW queries (Q and dO in registers), looping
+//   bwd_dq    one workgroup per 32*NW queries (Q and dO in registers; under
+//             causal masking the last, heaviest query tiles are issued first), looping
 //             over 64-key tiles of K and V in LDS: S^T = K Q^T and
 //             dP^T = V dO^T put a query in each lane's column, the B-operand
 //             layout of dQ^T += K^T dS^T (K^T read transposed from LDS).
@@ -156,39 +157,44 @@ bwd_dkdv(BwdParams p)
         __syncthreads();
         if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
 
-        // S = Q K^T and dP = dO V^T: lane holds key column `col`, query rows
-        // 8*(j/4) + 4*hh + j%4 of the 32-query tile
-        f32x16 s = (f32x16){}, dp = (f32x16){};
+        // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
+        f32x16 s = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
             const u32x4 qa = sq[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
-            const u32x4 ga = sg[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
             s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
-            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, vw[ks]), dp);
         }
-        // P = exp2(s*c - lse2) (0 for masked pairs); dS = P (dP - D)
-        f32x16 pp, dsv;
+        // P = exp2(s*c - lse2), 0 for masked pairs (in place), rounded copy for dV
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int qr = 8 * (j >> 2) + 4 * hh + (j & 3);
             const int qi = q0 + qr;
             bool vis = key_on && qi < N;
             if (p.causal) vis = vis && key <= qi;
-            const float pv = vis ? fast_exp2(fmaf(s[j], c, -s_l2[buf][qr])) : 0.f;
-            pp[j] = pv;
-            dsv[j] = pv * (dp[j] - s_d[buf][qr]);
+            s[j] = vis ? fast_exp2(fmaf(s[j], c, -s_l2[buf][qr])) : 0.f;
         }
-        // dV += P^T dO and dK += dS^T Q, contraction over the 32 queries
+        const v8 pa0 = pack8<T>(s, 0), pa1 = pack8<T>(s, 1);
+        // dV += P^T dO (contraction over the 32 queries)
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            const v8 pa = pack8<T>(pp, ks2), da = pack8<T>(dsv, ks2);
+        for (int db = 0; db < DB; ++db) {
+            dv[db] = TR::mma32(pa0, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 0, db, lane)), dv[db]);
+            dv[db] = TR::mma32(pa1, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 1, db, lane)), dv[db]);
+        }
+        // dP = dO V^T, then dS = P (dP - D) in place
+        f32x16 dp = (f32x16){};
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x4 gb = tr_operand<CPR>(sg[buf], ks2, db, lane);
-                const u32x4 qb = tr_operand<CPR>(sq[buf], ks2, db, lane);
-                dv[db] = TR::mma32(pa, __builtin_bit_cast(v8, gb), dv[db]);
-                dk[db] = TR::mma32(da, __builtin_bit_cast(v8, qb), dk[db]);
-            }
+        for (int ks = 0; ks < DK; ++ks) {
+            const u32x4 ga = sg[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
+            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, vw[ks]), dp);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - s_d[buf][8 * (j >> 2) + 4 * hh + (j & 3)]);
+        const v8 da0 = pack8<T>(dp, 0), da1 = pack8<T>(dp, 1);
+        // dK += dS^T Q
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            dk[db] = TR::mma32(da0, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 0, db, lane)), dk[db]);
+            dk[db] = TR::mma32(da1, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 1, db, lane)), dk[db]);
         }
     }
 
@@ -225,7 +231,8 @@ bwd_dq(BwdParams p)
     const int hh = lane >> 5, col = lane & 31;
     const int N = p.N;
     const int bh = blockIdx.x % (p.B * p.H);
-    const int qt = blockIdx.x / (p.B * p.H);
+    int qt = blockIdx.x / (p.B * p.H);
+    if (p.causal) qt = (N + 32 * NW - 1) / (32 * NW) - 1 - qt;   // heaviest query tiles first
     const int b = bh / p.H;
     const size_t head = (size_t)bh * N * D;
     const T* __restrict__ Q = (const T*)p.q + head;
