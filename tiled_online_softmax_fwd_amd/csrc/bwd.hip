@@ -142,20 +142,34 @@ bwd_dkdv(BwdParams p)
         plan.issue(sq[buf], Q, qt * BQ, N, wave);
         plan.issue(sg[buf], G, qt * BQ, N, wave);
     };
-    if (qt0 < nqt) stage(0, qt0);
+    // lse2 and D of a query tile: loaded into registers one tile ahead by the
+    // first BQ threads, stored to LDS at the top of the tile's step
+    float nl2 = 0.f, nd = 0.f;
+    auto row_terms = [&](int qt) __attribute__((always_inline)) {
+        const int qi = qt * BQ + (int)threadIdx.x;
+        const int qr = min(qi, N - 1);
+        nl2 = qi < N ? L2[qr] : INFINITY;
+        nd = DS[qr];
+    };
+    if (qt0 < nqt) {
+        stage(0, qt0);
+        if (threadIdx.x < BQ) row_terms(qt0);
+    }
 
     for (int qt = qt0; qt < nqt; ++qt) {
         const int buf = (qt - qt0) & 1;
         const int q0 = qt * BQ;
         // tile qt landed; every wave is done with tile qt-1 (other buffer)
         if (threadIdx.x < BQ) {
-            const int qr = min(q0 + (int)threadIdx.x, N - 1);
-            s_l2[buf][threadIdx.x] = (q0 + (int)threadIdx.x < N) ? L2[qr] : INFINITY;
-            s_d[buf][threadIdx.x] = DS[qr];
+            s_l2[buf][threadIdx.x] = nl2;
+            s_d[buf][threadIdx.x] = nd;
         }
         wait_vmcnt<0>();
         __syncthreads();
-        if (qt + 1 < nqt) stage(buf ^ 1, qt + 1);
+        if (qt + 1 < nqt) {
+            stage(buf ^ 1, qt + 1);
+            if (threadIdx.x < BQ) row_terms(qt + 1);
+        }
 
         // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
         f32x16 s = (f32x16){};
