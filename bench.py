@@ -13,6 +13,10 @@ duration per launch against the bf16 matrix-core peak), and the fp64 oracle
 timed on the host cores on a bounded row sample of the same workload; the
 sampled rows also give max/mean/std |delta| of the timed launch's output
 against the fp64 definition.
+
+Other modes (not the headline): --workload decode times attn_decode_fwd (a
+query block against a key/value cache; priced against HBM bandwidth) and
+--workload backward times attn_bwd (the gradient; 2.5x the forward's FLOPs).
 """
 import argparse
 import hashlib

@@ -23,6 +23,12 @@
  * A row with no visible key has no softmax; this library defines its output as
  * +0.0 in every element and lse = -infinity.
  *
+ * Entry points: the forward (attn_fwd, attn_fwd_ex, with host-only checks in
+ * attn_check_args), the materialising baseline (attn_naive_fwd), a query
+ * block against a key/value cache (attn_decode_fwd) and the gradient
+ * (attn_bwd).  The last three take a caller-owned device workspace whose size
+ * their *_workspace_bytes function gives.
+ *
  * Conventions shared by every entry point below:
  *   - q, k, v, o: DEVICE pointers, contiguous [B][H][N][d] row-major, element
  *     type given by `dtype` (see attn_dtype), 16-byte aligned.  The caller owns
