@@ -88,9 +88,11 @@ enum attn_status {
 /* Tile and fold-order options (attn_fwd_ex).
  *   br: query rows per workgroup tile, one of 16, 32, 64, 128, or 256 for the
  *       16-bit types with bc in {32, 64, 128} at d = 128 or bc = 64 at d = 64
- *       (0 = default: 256 for the 16-bit types and 128 for fp32; 128 when
- *       only bc is given and no 256-row tile exists for it).
- *   bc: keys per key tile, one of 16, 32, 64, 128 (0 = default).  bc is also the
+ *       (0 = default: 256 for the 16-bit types at d = 128, 128 at d = 64
+ *       and for fp32; 128 when only bc is given and no 256-row tile exists
+ *       for it).
+ *   bc: keys per key tile, one of 16, 32, 64, 128 (0 = default: 128 for the
+ *       16-bit types at d = 64, 64 otherwise).  bc is also the
  *       rescaling granularity: the running maximum is updated once per tile.
  *   kv_order: 0 folds each row's key tiles first to last, 1 last to first.
  *   ref_slack: 0 (default) keeps the reference of the online merge at each

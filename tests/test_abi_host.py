@@ -38,6 +38,7 @@ def test_version_and_status_strings():
 
 def test_default_tiles():
     assert A.default_tiles(A.BF16, 128, True) == (256, 64)
+    assert A.default_tiles(A.F16, 64, True) == (128, 128)
     assert A.default_tiles(A.F32, 64, False) == (128, 64)
     with pytest.raises(A.AttnError):
         A.default_tiles(A.BF16, 96)

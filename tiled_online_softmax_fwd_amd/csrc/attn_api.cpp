@@ -47,14 +47,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 bool valid_tile(int t) { return t == 16 || t == 32 || t == 64 || t == 128; }
 bool valid_br(int t) { return valid_tile(t) || t == 256; }
 
-// Defaults per input type: 16-bit inputs use 256 query rows per workgroup
-// (eight waves of 32 rows, sharing each K/V tile) and 64 keys per tile; fp32
-// uses 128 rows (its tiles are twice as large in LDS).
+// Defaults per input type and head size (measured on MI355X): 16-bit inputs
+// at d = 128 use 256 query rows per workgroup (eight waves of 32 rows sharing
+// each K/V tile) and 64 keys per tile; at d = 64 the state is half as large and
+// 128 x 128 tiles run best (three workgroups per compute unit); fp32 uses
+// 128 x 64 (its tiles are twice as large in LDS).
 void defaults(int dtype, int d, int causal, int* br, int* bc)
 {
-    (void)d; (void)causal;
-    *br = dtype == ATTN_F32 ? 128 : 256;
-    *bc = 64;
+    (void)causal;
+    if (dtype == ATTN_F32) { *br = 128; *bc = 64; }
+    else if (d == 64) { *br = 128; *bc = 128; }
+    else { *br = 256; *bc = 64; }
 }
 
 attnk::LaunchFn find(int dtype, int d, int br, int bc)
