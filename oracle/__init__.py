@@ -36,10 +36,11 @@ def _load():
         lib.oracle_row_blocked_f64.argtypes = [_D, _D, _U8, L, L, L, I, I, _D, _D]
         lib.oracle_attn_kv_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, L, D, I, _U8]
         lib.oracle_attn_bwd_f64.argtypes = [_D, _D, _D, _D, _D, _D, _D, L, L, L, L, D, I, _U8]
+        lib.oracle_attn_blockmask_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, D, I, _U8, _U8, L]
         lib.oracle_num_threads.argtypes = []
         for f in (lib.oracle_attn_f64, lib.oracle_attn_rows_f64, lib.oracle_attn_blocked_f64,
                   lib.oracle_attn_blocked_kvouter_f64, lib.oracle_row_softmax_f64,
-                  lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64, lib.oracle_attn_bwd_f64):
+                  lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_blockmask_f64):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -180,6 +181,23 @@ def attn_bwd(q, k, v, dout, scale, causal=False, mask=None):
     _check(_load().oracle_attn_bwd_f64(qp, kp, vp, gp, dq.ctypes.data_as(_D), dk.ctypes.data_as(_D),
                                        dv.ctypes.data_as(_D), B, H, N, d, float(scale), int(bool(causal)), mp))
     return dq, dk, dv
+
+
+def attn_blockmask(q, k, v, scale, block_mask, block=64, causal=False, mask=None):
+    """Plain definition with block-sparse visibility: block_mask [B,H,nb,nb]
+    (nb = ceil(N / block)), non-zero = the block of pairs is attended."""
+    keep, (qp, kp, vp) = _qkv(q, k, v)
+    B, H, N, d = keep[0].shape
+    nb = (N + block - 1) // block
+    bm = np.ascontiguousarray(block_mask, dtype=np.uint8)
+    if bm.shape != (B, H, nb, nb):
+        raise ValueError(f"block_mask must be [B, H, {nb}, {nb}]")
+    mk, mp = _mask(mask, B, N)
+    o = np.empty((B, H, N, d), np.float64)
+    lse = np.empty((B, H, N), np.float64)
+    _check(_load().oracle_attn_blockmask_f64(qp, kp, vp, o.ctypes.data_as(_D), lse.ctypes.data_as(_D), B, H, N, d,
+                                             float(scale), int(bool(causal)), mp, bm.ctypes.data_as(_U8), int(block)))
+    return o, lse
 
 
 def num_threads():

@@ -157,6 +157,56 @@ int oracle_attn_rows_f64(const double* q, const double* k, const double* v,
 }
 
 /*
+ * Block-sparse visibility (the yadro-code tutorial names a block-sparse
+ * variant of FlashAttention without describing it; this library's reading):
+ * on top of causal and key-padding visibility, the pair (i, j) is visible only
+ * if bmask[((b*H + h)*nqb + i/bs)*nkb + j/bs] != 0, with blocks of bs x bs
+ * and nqb = nkb = ceil(N / bs).  Plain definition otherwise, as
+ * oracle_attn_f64 (rows with nothing visible give 0 and -inf).
+ */
+int oracle_attn_blockmask_f64(const double* q, const double* k, const double* v,
+                              double* o, double* lse, long B, long H, long N, long d,
+                              double scale, int causal, const unsigned char* mask,
+                              const unsigned char* bmask, long bs)
+{
+    if (bad_sizes(B, H, N, d) || !o || !lse || !bmask || bs <= 0) return -1;
+    const long nb = (N + bs - 1) / bs;
+    const long rows = B * H * N;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (long r = 0; r < rows; ++r) {
+            const long i = r % N, bh = r / N, b = bh / H;
+            const double* qi = q + r * d;
+            const unsigned char* brow = bmask + (bh * nb + i / bs) * nb;
+            double m = -INFINITY;
+            int any = 0;
+            for (long j = 0; j < N; ++j) {
+                if (!visible(b, i, j, N, causal, mask) || !brow[j / bs]) { s[j] = -INFINITY; continue; }
+                s[j] = score(qi, k + (bh * N + j) * d, d, scale);
+                if (!any || s[j] > m) m = s[j];
+                any = 1;
+            }
+            double* orow = o + r * d;
+            for (long c = 0; c < d; ++c) orow[c] = 0.0;
+            if (!any) { lse[r] = -INFINITY; continue; }
+            double l = 0.0;
+            for (long j = 0; j < N; ++j) {
+                if (s[j] == -INFINITY) continue;
+                const double w = exp(s[j] - m);
+                l += w;
+                for (long c = 0; c < d; ++c) orow[c] += w * v[(bh * N + j) * d + c];
+            }
+            for (long c = 0; c < d; ++c) orow[c] /= l;
+            lse[r] = m + log(l);
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
  * Gradient of the plain definition (reverse mode of softmax(scale q k^T) v),
  * written out from the definition with the chain rule: for one (b, h), with
  * P the row softmax over visible keys and O = P V,

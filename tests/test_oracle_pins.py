@@ -471,3 +471,42 @@ def test_gradient_sum_rules():
     mask = np.zeros((2, 17), np.uint8); mask[1, :] = 1
     dq, dk, dv = oracle.attn_bwd(q, k, v, g, 0.4, False, mask)
     assert np.all(dq[1] == 0) and np.all(dk[1] == 0) and np.all(dv[1] == 0)
+
+
+# ------------------------------------------------------- block-sparse visibility
+def test_block_mask_matches_brute_force():
+    """Block-sparse reading: pair (i, j) visible iff causal/padding allow it and
+    its block is on; against the brute-force definition with the equivalent
+    element mask built in Python."""
+    rng = np.random.default_rng([44, 0])
+    B, H, N, d, bs = 2, 2, 11, 3, 4
+    q, k, v = (rng.integers(-3, 4, (B, H, N, d)).astype(np.float64) for _ in range(3))
+    nb = (N + bs - 1) // bs
+    bm = (rng.random((B, H, nb, nb)) < 0.6).astype(np.uint8)
+    bm[0, 0, 1, :] = 0                                  # a whole row block off
+    for causal in (False, True):
+        o, lse = oracle.attn_blockmask(q, k, v, 0.5, bm, bs, causal)
+        for b in range(B):
+            for h in range(H):
+                for i in range(N):
+                    cols = [j for j in range(N) if (not causal or j <= i) and bm[b, h, i // bs, j // bs]]
+                    if not cols:
+                        assert np.all(o[b, h, i] == 0) and lse[b, h, i] == -math.inf
+                        continue
+                    s = {j: 0.5 * math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in cols}
+                    top = max(s.values())
+                    w = {j: math.exp(s[j] - top) for j in cols}
+                    tot = math.fsum(w.values())
+                    ref = [math.fsum(w[j] * v[b, h, j, c] for j in cols) / tot for c in range(d)]
+                    np.testing.assert_allclose(o[b, h, i], ref, rtol=1e-13, atol=1e-13)
+                    assert math.isclose(lse[b, h, i], top + math.log(tot), rel_tol=1e-14, abs_tol=1e-13)
+
+
+def test_all_blocks_on_is_the_dense_definition():
+    rng = np.random.default_rng([45, 0])
+    q, k, v = (rng.standard_normal((1, 2, 150, 8)) for _ in range(3))
+    bm = np.ones((1, 2, 3, 3), np.uint8)
+    for causal in (False, True):
+        o, l = oracle.attn_blockmask(q, k, v, 0.3, bm, 64, causal)
+        od, ld = oracle.attn(q, k, v, 0.3, causal)
+        assert np.array_equal(o, od) and np.array_equal(l, ld)
