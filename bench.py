@@ -16,7 +16,9 @@ against the fp64 definition.
 
 Other modes (not the headline): --workload decode times attn_decode_fwd (a
 query block against a key/value cache; priced against HBM bandwidth) and
---workload backward times attn_bwd (the gradient; 2.5x the forward's FLOPs).
+--workload backward times attn_bwd (the gradient; 2.5x the forward's FLOPs),
+--workload sparse times attn_fwd_sparse (block-sparse flags, FLOPs counted over
+the attended pairs only).
 """
 import argparse
 import hashlib
@@ -82,9 +84,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
     ap.add_argument("--naive", action="store_true", help="also time the materialising baseline")
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "backward"],
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "backward", "sparse"],
                     help="prefill: the causal forward (default); decode: Nq query rows against a key/value "
-                         "cache; backward: gradient of the forward")
+                         "cache; backward: gradient of the forward; sparse: block-sparse forward")
+    ap.add_argument("--pattern", default="local_global", choices=["local_global", "random"],
+                    help="sparse: block flags (sliding window of blocks plus global blocks, or i.i.d.)")
+    ap.add_argument("--block", type=int, default=64, help="sparse: block edge")
+    ap.add_argument("--band", type=int, default=4, help="sparse local_global: window half-width in blocks")
+    ap.add_argument("--n-global", type=int, default=1, help="sparse local_global: global row/column blocks")
+    ap.add_argument("--density", type=float, default=0.5, help="sparse random: fraction of blocks on")
     ap.add_argument("--Nq", type=int, default=1, help="decode: query rows per head")
     ap.add_argument("--Nk", type=int, default=8192, help="decode: cached keys per head")
     ap.add_argument("--decode-B", type=int, default=8, help="decode: batch")
@@ -122,6 +130,8 @@ def main():
         return run_decode(args, torch, synth, A)
     if args.workload == "backward":
         return run_backward(args, torch, synth, A)
+    if args.workload == "sparse":
+        return run_sparse(args, torch, synth, A)
 
     B, H, N, d = args.B, args.H, args.N, args.d
     causal = not args.no_causal
@@ -311,6 +321,102 @@ def run_backward(args, torch, synth, A):
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "bwd_pre + bwd_dkdv + bwd_dq",
+                     "kernel_ms_mean": float(kms.mean())},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def attended_pairs(bm, N, block, causal):
+    """Number of (row, key) pairs the block flags bm [B, H, nb, nb] switch on,
+    after causality (counting only)."""
+    nb = bm.shape[-1]
+    starts = np.arange(nb) * block
+    width = np.minimum(block, N - starts)                         # keys per key block
+    if causal:
+        i = np.arange(N)[:, None]
+        per_row = np.clip(i - starts[None, :] + 1, 0, width[None, :])   # [N, nb]
+        per_block = np.add.reduceat(per_row, starts, axis=0)            # [nb(row), nb(key)]
+    else:
+        per_block = np.minimum(block, N - starts)[:, None] * width[None, :]
+    return int((bm.astype(np.int64) * per_block[None, None]).sum())
+
+
+def run_sparse(args, torch, synth, A):
+    """Block-sparse forward on the prefill shape; algorithmic work is 4*d FLOPs
+    per attended (row, key) pair."""
+    B, H, N, d = args.B, args.H, args.N, args.d
+    if args.dtype == "f32":
+        print("the block-sparse forward takes 16-bit inputs", file=sys.stderr)
+        sys.exit(2)
+    causal = not args.no_causal
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    blk = args.block
+    bm = synth.block_mask(B, H, N, blk, 5, args.pattern, args.density, args.band, args.n_global)
+    pairs = attended_pairs(bm, N, blk, causal)
+    pat = (f"window +-{args.band} blocks + {args.n_global} global" if args.pattern == "local_global"
+           else f"random density {args.density}")
+    print(f"[bench] sparse B{B} H{H} N{N} d{d} {args.dtype} block {blk} {pat}, "
+          f"{pairs / (B * H * N * N):.4f} of all pairs", file=sys.stderr, flush=True)
+    p = synth.make_qkv(B, H, N, d, args.dtype, 5)
+    q, k, v = synth.upload(p)
+    bmt = torch.from_numpy(bm).cuda()
+    out = torch.empty((B, H, N, d), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.fwd_sparse(q, k, v, bmt, block=blk, scale=scale, causal=causal, out=out, lse=lse,
+                     br=args.br or None, bc=args.bc or None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    fl = 4.0 * d * pairs
+    tf = fl / (kms.mean() * 1e-3) / 1e12
+    print(f"[bench] sparse {args.steps} steps: mean {kms.mean():.4f} ms, {tf:.0f} TFLOP/s", file=sys.stderr)
+    check = None
+    if not args.no_cpu:
+        import oracle
+        rows = synth.sample_rows(B, H, N, 4, 11)
+        o64 = out.to(torch.float64).cpu().numpy()
+        l64 = lse.to(torch.float64).cpu().numpy()
+        errs, lerr = [], []
+        t = time.perf_counter()
+        for r in rows:
+            bh, i = divmod(int(r), N)
+            b, h = divmod(bh, H)
+            vis = np.repeat(bm[b, h, i // blk], blk)[:N].astype(bool)
+            if causal:
+                vis &= np.arange(N) <= i
+            sl = slice(h, h + 1)
+            ro, rl = oracle.attn_rows(p.q64[b:b + 1, sl], p.k64[b:b + 1, sl], p.v64[b:b + 1, sl], scale,
+                                      np.array([i]), False, (~vis).astype(np.uint8)[None, :])
+            errs.append(np.abs(o64[b, h, i] - ro[0]))
+            if np.isfinite(rl[0]):
+                lerr.append(abs(l64[b, h, i] - rl[0]))
+        e = np.concatenate(errs) if errs else np.zeros(1)
+        check = {"rows_checked": int(len(rows)), "time_s": time.perf_counter() - t, "max_abs": float(e.max()),
+                 "mean_abs": float(e.mean()), "lse_max_abs": float(max(lerr) if lerr else 0.0)}
+    line = {
+        "metric": "block-sparse attention fwd TFLOP/s over attended pairs", "value": fl / (wall / args.steps) / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"block-sparse B{B} H{H} N{N} d{d} {args.dtype} {'causal' if causal else 'non-causal'}, "
+                               f"block {blk}, {pat}", "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "attended_fraction": pairs / (B * H * N * N)},
+        "check_vs_fp64_oracle": check,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "fwd_m32_h16 (block-sparse)",
                      "kernel_ms_mean": float(kms.mean())},
     }
     print(json.dumps(line), flush=True)

@@ -24,7 +24,7 @@
  * +0.0 in every element and lse = -infinity.
  *
  * Entry points: the forward (attn_fwd, attn_fwd_ex, with host-only checks in
- * attn_check_args), the materialising baseline (attn_naive_fwd), a query
+ * attn_check_args), its block-sparse variant (attn_fwd_sparse), the materialising baseline (attn_naive_fwd), a query
  * block against a key/value cache (attn_decode_fwd) and the gradient
  * (attn_bwd).  The last three take a caller-owned device workspace whose size
  * their *_workspace_bytes function gives.
@@ -124,6 +124,30 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int H, int N, int d, float scale, int causal,
                 const uint8_t* key_padding_mask, int dtype, void* stream,
                 const attn_opts* opts);
+
+/* Block-sparse forward.  The yadro-code tutorial ("How FlashAttention reduces
+ * GPU memory traffic", its overview of the NeurIPS 2022 paper) names a
+ * block-sparse extension without describing it; this library's reading: the
+ * rows and keys of each (b, h) are cut into blocks of `block` rows, and the
+ * pair (i, j) is visible only if block_mask[((b*H + h)*nb + i/block)*nb +
+ * j/block] is non-zero (nb = ceil(N / block)), in addition to the causal and
+ * key-padding rules of attn_fwd.  Everything else (softmax over the visible
+ * keys, empty rows -> 0 and -inf, lse) is attn_fwd's.  Key tiles without an
+ * attended block are skipped: the work scales with the attended blocks.
+ *   block_mask: DEVICE pointer to [B][H][nb][nb] bytes, caller-owned; must not
+ *       overlap o or lse.
+ *   block: a positive multiple of 32 (else ATTN_ERR_SHAPE).
+ *   dtype: the 16-bit types and their *_OUT_F32 flavours (ATTN_F32 ->
+ *       ATTN_ERR_DTYPE).
+ *   opts: as attn_fwd_ex, with (br, bc) one of (64, 64), (128, 64),
+ *       (128, 128), (256, 64) and kv_order 0; else ATTN_ERR_TILE.  Unset br
+ *       or bc (0, or opts NULL) default to 128 and 64: wider workgroups
+ *       visit tiles in which only some of their row blocks attend.
+ * Errors and stream semantics as attn_fwd. */
+int attn_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, const uint8_t* block_mask, int block,
+                    int dtype, void* stream, const attn_opts* opts);
 
 /* Host-only argument check of attn_fwd_ex: returns the status attn_fwd_ex would
  * return before launching anything.  Touches no device and no pointer. */

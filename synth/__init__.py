@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for attention tests and benchmarks.
 
 This module holds no attention arithmetic.  It draws i.i.d. normal Q, K, V (the
-pages' experiments use "the same randomly initialised" query, key and value
+pages' experiments reuse one set of randomly initialised query, key and value
 tensors and state no distribution, so N(0, 1) is used), rounds them to the
 storage type, and returns both the stored bits and their exact fp64 widening.
 Both the HIP library (through the stored bits) and the CPU oracle (through the
@@ -152,3 +152,25 @@ def sample_rows(B: int, H: int, N: int, per_head: int = 24, seed: int = 0) -> np
         pick.update(int(x) for x in rng.integers(0, N, size=per_head))
         rows.extend(bh * N + i for i in sorted(pick) if 0 <= i < N)
     return np.array(rows, np.int64)
+
+
+def block_mask(B: int, H: int, N: int, block: int, config_id: int, pattern: str = "random",
+               density: float = 0.5, band: int = 1, n_global: int = 1) -> np.ndarray:
+    """[B, H, nb, nb] uint8 block flags (1 = the block of pairs is attended),
+    nb = ceil(N / block), for the block-sparse forward.
+
+    pattern "random": each flag i.i.d. Bernoulli(density) from the stream
+    default_rng([config_id, N, 98]).  pattern "local_global": block (i, j) is on
+    if |i - j| <= band (a sliding window of blocks) or i < n_global or
+    j < n_global (global rows and columns), the same for every (b, h).
+    """
+    nb = (int(N) + int(block) - 1) // int(block)
+    if pattern == "random":
+        rng = np.random.default_rng([int(config_id), int(N), 98])
+        return (rng.random((B, H, nb, nb)) < density).astype(np.uint8)
+    if pattern == "local_global":
+        i = np.arange(nb)[:, None]
+        j = np.arange(nb)[None, :]
+        on = (np.abs(i - j) <= band) | (i < n_global) | (j < n_global)
+        return np.broadcast_to(on.astype(np.uint8), (B, H, nb, nb)).copy()
+    raise ValueError(f"unknown pattern {pattern!r}")

@@ -132,3 +132,27 @@ def test_decode_argument_checks():
     assert dec(ws=ctypes.c_void_p(0x20000 + 64)) == ALIAS    # inside k
     assert dec(o=ctypes.c_void_p(0x10000)) == ALIAS          # o == q
     assert dec(Nq=0, q=None, o=None) == OK                                          # empty: no-op
+
+
+def test_sparse_argument_checks():
+    """attn_fwd_sparse rejects, before any launch: fp32 inputs, a block that is
+    not a positive multiple of 32, kv_order 1, a tile without a block-sparse
+    instance, a NULL block_mask, and o overlapping the flags."""
+    L = A.lib()
+    base = 1 << 20
+    q, k, v, o, lse, bm = base, base + (1 << 24), base + (2 << 24), base + (3 << 24), base + (4 << 24), base + (5 << 24)
+
+    def call(dtype=A.BF16, block=64, opts=None, bmask=bm, N=256, d=128, oo=o):
+        return L.attn_fwd_sparse(q, k, v, oo, lse, 1, 2, N, d, 0.1, 0, None, bmask, block, dtype, None,
+                                 ctypes.byref(opts) if opts is not None else None)
+
+    assert call(dtype=A.F32) == DTYPE
+    for blk in (0, -64, 16, 48, 100):
+        assert call(block=blk) == SHAPE, blk
+    assert call(opts=A.make_opts(kv_order=1)) == TILE
+    for br, bc in ((32, 32), (64, 128), (256, 128), (16, 64), (128, 32)):
+        assert call(opts=A.make_opts(br, bc)) == TILE, (br, bc)
+    assert call(bmask=None) == NULL
+    assert call(bmask=o + 64) == ALIAS
+    assert call(d=96) == HEAD
+    assert call(N=0, bmask=None) == OK          # empty problem: no-op before any pointer check

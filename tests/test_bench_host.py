@@ -1,0 +1,30 @@
+"""Host-side logic of bench.py and the block-flag generator (no GPU)."""
+import numpy as np
+
+import bench
+import synth
+
+
+def test_attended_pairs_against_brute_force():
+    for N, blk, causal in ((300, 64, True), (300, 64, False), (777, 96, True), (128, 32, True), (65, 64, True)):
+        bm = synth.block_mask(2, 2, N, blk, 3, "random", 0.4)
+        tot = 0
+        for b in range(2):
+            for h in range(2):
+                f = np.repeat(np.repeat(bm[b, h], blk, 0), blk, 1)[:N, :N].astype(bool)
+                if causal:
+                    f &= np.tril(np.ones((N, N), bool))
+                tot += int(f.sum())
+        assert bench.attended_pairs(bm, N, blk, causal) == tot, (N, blk, causal)
+
+
+def test_block_mask_patterns():
+    bm = synth.block_mask(1, 2, 1000, 64, 1, "local_global", band=2, n_global=1)
+    assert bm.shape == (1, 2, 16, 16) and bm.dtype == np.uint8
+    i, j = np.indices((16, 16))
+    want = ((np.abs(i - j) <= 2) | (i < 1) | (j < 1)).astype(np.uint8)
+    assert np.array_equal(bm[0, 0], want) and np.array_equal(bm[0, 1], want)
+    r1 = synth.block_mask(2, 3, 500, 32, 7, "random", 0.3)
+    r2 = synth.block_mask(2, 3, 500, 32, 7, "random", 0.3)
+    assert np.array_equal(r1, r2) and r1.shape == (2, 3, 16, 16)
+    assert 0.2 < r1.mean() < 0.4

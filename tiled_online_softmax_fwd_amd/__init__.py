@@ -16,7 +16,7 @@ F32, F16, BF16, F16_OUT_F32, BF16_OUT_F32 = 0, 1, 2, 3, 4
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HEAD_DIM",
           4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_TILE", 7: "ATTN_ERR_SCALE",
           8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
-EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_sparse", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
            "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes",
            "attn_bwd", "attn_bwd_workspace_bytes",
            "attn_status_string", "attn_last_error", "attn_version")
@@ -49,6 +49,7 @@ def lib():
         L.attn_fwd.argtypes = common + [vp]
         L.attn_fwd_ex.argtypes = common + [vp, ctypes.POINTER(attn_opts)]
         L.attn_check_args.argtypes = common + [ctypes.POINTER(attn_opts)]
+        L.attn_fwd_sparse.argtypes = common[:12] + [vp, i, i, vp, ctypes.POINTER(attn_opts)]
         L.attn_default_tiles.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
         L.attn_naive_fwd.argtypes = common + [vp, vp, ctypes.c_size_t]
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
@@ -64,7 +65,7 @@ def lib():
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
-        for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_check_args, L.attn_default_tiles,
+        for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_fwd_sparse, L.attn_check_args, L.attn_default_tiles,
                    L.attn_naive_fwd, L.attn_decode_fwd, L.attn_bwd, L.attn_version):
             fn.restype = ctypes.c_int
         _lib = L
@@ -142,6 +143,30 @@ def fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=None, l
     opts = make_opts(br, bc, kv_order, ref_slack)
     st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                            int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s), ctypes.byref(opts))
+    _raise(st)
+    return out, lse
+
+
+def fwd_sparse(q, k, v, block_mask, *, block=64, scale=None, causal=False, key_padding_mask=None, out=None,
+               lse=None, out_fp32=False, br=None, bc=None, ref_slack=0, want_lse=True, stream=None):
+    """Block-sparse forward through attn_fwd_sparse: block_mask is a
+    [B, H, ceil(N / block), ceil(N / block)] uint8/bool GPU tensor (non-zero =
+    the block of pairs is attended).  Returns (out, lse)."""
+    torch = _torch()
+    B, H, N, d, code, out, lse, mask = _prep(q, k, v, key_padding_mask, out, lse, out_fp32, want_lse)
+    nb = (N + int(block) - 1) // int(block) if block and int(block) > 0 else 0
+    if block_mask.dtype not in (torch.uint8, torch.bool) or tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError(f"block_mask must be a [B, H, {nb}, {nb}] uint8/bool tensor")
+    if not block_mask.is_cuda:
+        raise ValueError("block_mask must be a GPU tensor")
+    block_mask = block_mask.contiguous()
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
+    opts = make_opts(br, bc, 0, ref_slack)
+    st = lib().attn_fwd_sparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
+                               int(bool(causal)), _ptr(mask), _ptr(block_mask), int(block), code,
+                               ctypes.c_void_p(s), ctypes.byref(opts))
     _raise(st)
     return out, lse
 

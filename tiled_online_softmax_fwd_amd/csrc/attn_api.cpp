@@ -200,7 +200,59 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.kv_order = order;
     p.slack = (float)slack;
     p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
+    p.bmask = nullptr;
+    p.blk = 0;
+    p.nb = 0;
     const hipError_t e = find(dtype, d, br, bc)(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int attn_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* key_padding_mask, const uint8_t* block_mask, int block,
+                    int dtype, void* stream, const attn_opts* opts)
+{
+    int st = check_scalars(B, H, N, d, scale, dtype);
+    if (st) return st;
+    if (dtype == ATTN_F32) return fail(ATTN_ERR_DTYPE, "block-sparse forward: 16-bit inputs only");
+    if (block < 32 || block % 32 != 0) return fail(ATTN_ERR_SHAPE, "block=%d must be a positive multiple of 32", block);
+    int br, bc, order, slack;
+    st = resolve_opts(dtype, d, causal, opts, &br, &bc, &order, &slack);
+    if (st) return st;
+    if (order != 0) return fail(ATTN_ERR_TILE, "block-sparse forward: kv_order must be 0");
+    // default 128 x 64: with blocks of 64 rows, wider workgroups visit tiles
+    // where only some of their row blocks attend (measured on MI355X at
+    // B1 H32 N8192, d = 64 and 128, random and sliding-window flags)
+    if (!opts || opts->br == 0) br = 128;
+    if (!opts || opts->bc == 0) bc = 64;
+    const int bits = (dtype == ATTN_F16 || dtype == ATTN_F16_OUT_F32) ? 1 : 0;
+    const attnk::LaunchFn fn = attnk::lookup_sparse(bits, d, br, bc);
+    if (!fn) return fail(ATTN_ERR_TILE, "no block-sparse kernel for d=%d, br=%d, bc=%d", d, br, bc);
+    if ((int64_t)B * H * N == 0) return ok();
+    st = check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
+    if (st) return st;
+    if (!block_mask) return fail(ATTN_ERR_NULL, "block_mask must be non-NULL");
+    const int nb = (N + block - 1) / block;
+    const size_t nbm = (size_t)B * H * (size_t)nb * (size_t)nb;
+    const size_t nout = (size_t)B * H * N * d * elem_bytes_out(dtype);
+    if (overlaps(o, nout, block_mask, nbm) || overlaps(lse, lse ? (size_t)B * H * N * 4 : 0, block_mask, nbm))
+        return fail(ATTN_ERR_ALIAS, "o or lse overlaps block_mask");
+
+    attnk::FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask;
+    p.B = B; p.H = H; p.N = N;
+    p.n_qt = (N + br - 1) / br;
+    p.scale = scale;
+    p.c = (float)((double)scale * 1.4426950408889634);
+    p.causal = causal ? 1 : 0;
+    p.kv_order = 0;
+    p.slack = (float)slack;
+    p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
+    p.bmask = block_mask;
+    p.blk = block;
+    p.nb = nb;
+    const hipError_t e = fn(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
 }

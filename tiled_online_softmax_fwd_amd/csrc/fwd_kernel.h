@@ -54,6 +54,9 @@ struct FwdParams {
     int kv_order;          // 0 ascending key tiles, 1 descending
     int out_f32;           // o is float instead of the input type
     float slack;           // lag allowed to the merge reference (base-2 units, 0 = exact maximum)
+    const uint8_t* bmask;  // block-sparse kernels: [B][H][nb][nb] block flags, non-zero = attended
+    int blk;               // block edge in rows (multiple of 32)
+    int nb;                // ceil(N / blk)
 };
 
 typedef hipError_t (*LaunchFn)(const FwdParams&, hipStream_t);
@@ -293,11 +296,93 @@ template <> struct Dot2<_Float16> {
     { return __builtin_amdgcn_fdot2(a, (v2){(_Float16)1.0f, (_Float16)1.0f}, acc, false); }
 };
 
+// Block-sparse walk (the tutorial names a block-sparse extension of
+// FlashAttention without giving it; here the pair (i, j) is attended only if
+// the flag of block (i / blk, j / blk) of its head is non-zero, on top of
+// causality and key padding).  A workgroup visits, in ascending order, only
+// the key tiles in which some row block of the workgroup attends some key
+// block: tiles without an attended pair are neither copied nor computed.
+// Flags are read 64 tiles at a time, one tile per lane, and reduced with a
+// ballot: `act` bit j = tile base + j has an attended block for the
+// workgroup; own[kb] bit j = this wave's row block attends the key block of
+// 32-key sub-block kb of tile base + j.  The words come from ballots, so they
+// are wave-uniform, and every wave of the workgroup derives the same `act`:
+// all waves visit the same tiles and meet the same barriers.
+template <int BR, int BC>
+struct BlockScan {
+    static constexpr int NKB = BC / 32;
+    const uint8_t* flags;   // this head's [nb][nb] block flags
+    int nb, blk, N, kt_end, qb_lo, qb_hi, qb_w;
+    int base = -64;         // first tile of the loaded words
+    uint64_t act = 0;
+    uint64_t own[NKB];
+
+    __device__ __forceinline__ void init(const FwdParams& p, int bh, int q0, int wave_q0, int kt_end_)
+    {
+        nb = p.nb;
+        blk = p.blk;
+        N = p.N;
+        kt_end = kt_end_;
+        flags = p.bmask + (size_t)bh * nb * nb;
+        qb_lo = q0 / blk;
+        qb_hi = (min(q0 + BR, N) - 1) / blk;
+        qb_w = min(wave_q0, N - 1) / blk;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) own[kb] = 0;
+    }
+
+    __device__ __forceinline__ void load(int b0, int lane)
+    {
+        const int t = b0 + lane;
+        bool any = false;
+        bool w[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) w[kb] = false;
+        if (t < kt_end) {
+            const int k0 = t * BC;            // < N: t < kt_end
+            const int kb_lo = k0 / blk, kb_hi = (min(k0 + BC, N) - 1) / blk;
+            for (int qb = qb_lo; qb <= qb_hi; ++qb)
+                for (int kbl = kb_lo; kbl <= kb_hi; ++kbl) any = any || flags[(size_t)qb * nb + kbl] != 0;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int key = k0 + 32 * kb;
+                w[kb] = key < N && flags[(size_t)qb_w * nb + key / blk] != 0;
+            }
+        }
+        act = __builtin_amdgcn_ballot_w64(any);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) own[kb] = __builtin_amdgcn_ballot_w64(w[kb]);
+        base = b0;
+    }
+
+    // first tile >= from with an attended block, or kt_end
+    __device__ __forceinline__ int next(int from, int lane)
+    {
+        while (from < kt_end) {
+            const int b0 = from & ~63;
+            if (b0 != base) load(b0, lane);
+            const uint64_t w = act & (~0ull << (from - b0));
+            if (w) return b0 + (int)__builtin_ctzll(w);
+            from = b0 + 64;
+        }
+        return kt_end;
+    }
+
+    // sub-block flags (bit kb) of the wave for tile t, t in the loaded words
+    __device__ __forceinline__ unsigned bits(int t) const
+    {
+        unsigned r = 0;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) r |= (unsigned)((own[kb] >> (t - base)) & 1u) << kb;
+        return r;
+    }
+};
+
 // Waves per SIMD the 16-bit kernel is register-budgeted for: two for the
 // tiles whose state fits in 256 registers, one otherwise.
 template <int D, int BC> struct H16Occ { static constexpr int value = (D * BC <= 128 * 64) ? 2 : 1; };
 
-template <typename T, int D, int BR, int BC>
+template <typename T, int D, int BR, int BC, bool SPARSE>
 __global__ void __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(H16Occ<D, BC>::value)))
 fwd_m32_h16(FwdParams p)
 {
@@ -336,13 +421,23 @@ fwd_m32_h16(FwdParams p)
     const int order = p.kv_order;
     auto tile_at = [&](int it) { return order ? (kt_end - 1 - it) : it; };
 
+    // block-sparse: first tile with an attended block (kt_end if none)
+    BlockScan<BR, BC> scan;
+    int t0 = tile_at(0);
+    if constexpr (SPARSE) {
+        scan.init(p, bh, q0, q0 + wave * 32, kt_end);
+        t0 = scan.next(0, lane);
+    }
+
     // prologue: first K and V tiles in flight before Q is even loaded
     KPlan kplan;
     VPlan vplan;
     kplan.init(wave, lane);
     vplan.init(wave, lane);
-    kplan.issue(sk[0], K, tile_at(0) * BC, N, wave);
-    vplan.issue(sv[0], V, tile_at(0) * BC, N, wave);
+    if (!SPARSE || t0 < kt_end) {
+        kplan.issue(sk[0], K, t0 * BC, N, wave);
+        vplan.issue(sv[0], V, t0 * BC, N, wave);
+    }
 
     // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7].  The empty asm
     // consumes it here, so the compiler's wait for these loads sits before the
@@ -369,18 +464,27 @@ fwd_m32_h16(FwdParams p)
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     typedef __attribute__((address_space(3))) char lds_char;
 
-    // One key tile.  BUF (the buffer tile `it` lives in, it & 1) is a
-    // compile-time constant: the loop below is unrolled by two, so every LDS
-    // address is a fixed register plus an immediate offset.
-    auto body = [&](auto BUF, int it) {
+    // One key tile: the it-th of the fold order (dense), or the tile starting
+    // at key sk0 followed by the one at sk0next (-1: none) with the wave's
+    // sub-block flags `sub` (block-sparse).  BUF (the buffer the tile lives
+    // in, alternating) is a compile-time constant: the loops below are
+    // unrolled by two, so every LDS address is a fixed register plus an
+    // immediate offset.
+    auto body = [&](auto BUF, int it, int sk0, int sk0next, unsigned sub) {
         constexpr int buf = decltype(BUF)::value;
-        const int k0 = tile_at(it) * BC;
+        const int k0 = SPARSE ? sk0 : tile_at(it) * BC;
 
-        // tile it landed; every wave is done with iteration it-1, so the
-        // other buffer can be refilled with tile it+1
+        // this tile landed; every wave is done with the previous one, so the
+        // other buffer can be refilled with the next tile
         wait_vmcnt<0>();
         wg_barrier();
-        if (it + 1 < kt_end) {
+        if constexpr (SPARSE) {
+            if (sk0next >= 0) {
+                kplan.issue(sk[buf ^ 1], K, sk0next, N, wave);
+                vplan.issue(sv[buf ^ 1], V, sk0next, N, wave);
+            }
+            if (sub == 0) return;   // no attended pair for this wave's rows
+        } else if (it + 1 < kt_end) {
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
         }
@@ -402,15 +506,20 @@ fwd_m32_h16(FwdParams p)
         // k0 + 32*kb + 8*(j/4) + 4*hh + j%4.
         const bool diag = p.causal && k0 + BC - 1 > wave_q0;
         const bool tail = k0 + BC > N;
-        if (tail || p.mask) {
-            // ragged last tile or key padding: full visibility test
+        // block-sparse: some 32-key sub-block of the tile not attended by the
+        // wave's rows (never with tiles no wider than a block)
+        const bool part = SPARSE && sub != (1u << NKB) - 1u;
+        if (tail || p.mask || part) {
+            // ragged last tile, key padding or partly attended tile: full
+            // visibility test
             const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
+                const bool on = !SPARSE || ((sub >> kb) & 1u);
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    bool vis = key < N && (!p.causal || key <= qi);
+                    bool vis = on && key < N && (!p.causal || key <= qi);
                     if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
                     if (!vis) s[kb][j] = -INFINITY;
                 }
@@ -481,9 +590,22 @@ fwd_m32_h16(FwdParams p)
         }
     };
 
-    for (int it = 0; it < kt_end; it += 2) {
-        body(Int<0>{}, it);
-        if (it + 1 < kt_end) body(Int<1>{}, it + 1);
+    if constexpr (SPARSE) {
+        int t = t0;
+        while (t < kt_end) {
+            const unsigned st = scan.bits(t);
+            const int t1 = scan.next(t + 1, lane);
+            body(Int<0>{}, 0, t * BC, t1 < kt_end ? t1 * BC : -1, st);
+            if (t1 >= kt_end) break;
+            const unsigned st1 = scan.bits(t1);
+            t = scan.next(t1 + 1, lane);
+            body(Int<1>{}, 0, t1 * BC, t < kt_end ? t * BC : -1, st1);
+        }
+    } else {
+        for (int it = 0; it < kt_end; it += 2) {
+            body(Int<0>{}, it, 0, 0, 0u);
+            if (it + 1 < kt_end) body(Int<1>{}, it + 1, 0, 0, 0u);
+        }
     }
 
     // epilogue: O = acc / l, lse = m*scale + ln(l); empty rows -> (0, -inf)
@@ -663,11 +785,11 @@ fwd_m32_f32(FwdParams p)
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D, int BR, int BC>
+template <typename T, int D, int BR, int BC, bool SPARSE = false>
 hipError_t launch_h16(const FwdParams& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
-    hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
+    hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC, SPARSE>), dim3(grid), dim3(BR * 2), 0, st, p);
     return hipGetLastError();
 }
 
@@ -683,5 +805,7 @@ hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 LaunchFn lookup_bf16(int D, int BR, int BC);
 LaunchFn lookup_f16(int D, int BR, int BC);
 LaunchFn lookup_f32(int D, int BR, int BC);
+// Block-sparse 16-bit instances (bits: 0 bf16, 1 f16).
+LaunchFn lookup_sparse(int dtype_bits, int D, int BR, int BC);
 
 }  // namespace attnk

@@ -16,3 +16,7 @@
 #define ATTN_FWD_TILES_16(X, D) \
     X(D, 16, 16)  X(D, 16, 32)  X(D, 16, 64) X(D, 16, 128) \
     X(D, 32, 16)  X(D, 64, 16)  X(D, 128, 16)
+
+// Tiles with a block-sparse instance (16-bit inputs): the defaults and their
+// neighbours.
+#define ATTN_FWD_TILES_SPARSE(X, D) X(D, 64, 64) X(D, 128, 64) X(D, 128, 128) X(D, 256, 64)
