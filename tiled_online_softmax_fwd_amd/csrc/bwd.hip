@@ -94,8 +94,9 @@ bwd_dkdv(BwdParams p)
     using Plan = TilePlan<BQ, CPR, NW, 0>;
     __shared__ u32x4 sq[2][BQ * CPR];
     __shared__ u32x4 sg[2][BQ * CPR];
-    __shared__ float s_l2[2][BQ];
-    __shared__ float s_d[2][BQ];
+    __shared__ u32x4 s_vw[NW][DK][64];   // each wave's V^T operands (registers are short)
+    __shared__ __attribute__((aligned(16))) float s_l2[2][BQ];
+    __shared__ __attribute__((aligned(16))) float s_d[2][BQ];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -115,16 +116,19 @@ bwd_dkdv(BwdParams p)
     const int key = k_wave + col;                     // this lane's key
     const int krow = min(key, N - 1);
     const bool key_on = key < N && !(p.mask && p.mask[(size_t)b * N + krow]);
+    const bool keys_all_on = __builtin_amdgcn_ballot_w64(key_on) == ~0ull;   // wave-uniform
 
-    // K^T and V^T operands of this lane's key: head columns 16*ks + 8*hh + 0..7
-    u32x4 kw[DK], vw[DK];
+    // K^T and V^T operands of this lane's key: head columns 16*ks + 8*hh + 0..7.
+    // K^T stays in registers; V^T goes to the wave's own LDS slots (each lane
+    // reads back only what it wrote), which keeps the loop free of spills.
+    u32x4 kw[DK];
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
         kw[ks] = *(const u32x4*)(K + (size_t)krow * D + ks * 16 + hh * 8);
-        vw[ks] = *(const u32x4*)(V + (size_t)krow * D + ks * 16 + hh * 8);
+        s_vw[wave][ks][lane] = *(const u32x4*)(V + (size_t)krow * D + ks * 16 + hh * 8);
     }
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) { asm volatile("" : "+v"(kw[ks])); asm volatile("" : "+v"(vw[ks])); }
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(kw[ks]));
 
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -171,6 +175,10 @@ bwd_dkdv(BwdParams p)
             if (threadIdx.x < BQ) row_terms(qt + 1);
         }
 
+        // causal: every query of the tile precedes every key of the wave, so
+        // the wave has nothing to add (it still took part in the copy above)
+        if (p.causal && q0 + BQ - 1 < k_wave) continue;
+
         // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
         f32x16 s = (f32x16){};
 #pragma unroll
@@ -178,14 +186,28 @@ bwd_dkdv(BwdParams p)
             const u32x4 qa = sq[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
             s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
         }
-        // P = exp2(s*c - lse2), 0 for masked pairs (in place), rounded copy for dV
+        // lse2 of the lane's 16 query rows: four 16-byte LDS reads
+        f32x4 l2v[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) l2v[g4] = *(const f32x4*)&s_l2[buf][8 * g4 + 4 * hh];
+        // P = exp2(s*c - lse2).  Every exponential is formed (rows past the end
+        // carry lse2 = +inf and give 0); the empty asm keeps each one out of a
+        // per-element branch.  Pairs that are not visible are then set to 0,
+        // on tiles that are not wholly visible only.
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int qr = 8 * (j >> 2) + 4 * hh + (j & 3);
-            const int qi = q0 + qr;
-            bool vis = key_on && qi < N;
-            if (p.causal) vis = vis && key <= qi;
-            s[j] = vis ? fast_exp2(fmaf(s[j], c, -s_l2[buf][qr])) : 0.f;
+            s[j] = fast_exp2(fmaf(s[j], c, -l2v[j >> 2][j & 3]));
+            asm volatile("" : "+v"(s[j]));
+        }
+        const bool all = keys_all_on && q0 + BQ <= N && (!p.causal || q0 >= k_wave + 31);
+        if (!all) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int qi = q0 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                bool vis = key_on && qi < N;
+                if (p.causal) vis = vis && key <= qi;
+                s[j] = vis ? s[j] : 0.f;
+            }
         }
         const v8 pa0 = pack8<T>(s, 0), pa1 = pack8<T>(s, 1);
         // dV += P^T dO (contraction over the 32 queries)
@@ -199,10 +221,14 @@ bwd_dkdv(BwdParams p)
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
             const u32x4 ga = sg[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
-            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, vw[ks]), dp);
+            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][ks][lane]), dp);
         }
+        // D of the same rows, read where it is used
+        f32x4 dsv[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - s_d[buf][8 * (j >> 2) + 4 * hh + (j & 3)]);
+        for (int g4 = 0; g4 < 4; ++g4) dsv[g4] = *(const f32x4*)&s_d[buf][8 * g4 + 4 * hh];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - dsv[j >> 2][j & 3]);
         const v8 da0 = pack8<T>(dp, 0), da1 = pack8<T>(dp, 1);
         // dK += dS^T Q
 #pragma unroll
@@ -254,7 +280,8 @@ bwd_dq(BwdParams p)
     const T* __restrict__ V = (const T*)p.v + head;
     const T* __restrict__ G = (const T*)p.dout + head;
     const int q0 = qt * 32 * NW;
-    const int qi = q0 + wave * 32 + col;              // this lane's query
+    const int wave_q0 = q0 + wave * 32;
+    const int qi = wave_q0 + col;                     // this lane's query
     const int qrow = min(qi, N - 1);
     const float l2 = qi < N ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
     const float dsum = p.dsum[(size_t)bh * N + qrow];
@@ -291,6 +318,9 @@ bwd_dq(BwdParams p)
             plan.issue(sk[buf ^ 1], K, k0 + BC, N, wave);
             plan.issue(sv[buf ^ 1], V, k0 + BC, N, wave);
         }
+        // causal: every key of the tile follows every query of the wave
+        if (p.causal && k0 > wave_q0 + 31) continue;
+
         // S^T = K Q^T and dP^T = V dO^T: lane holds query column `col`, key
         // rows 32*kb + 8*(j/4) + 4*hh + j%4
         f32x16 s[NKB], dp[NKB];
@@ -307,19 +337,35 @@ bwd_dq(BwdParams p)
                 dp[kb] = TR::mma32(__builtin_bit_cast(v8, va), __builtin_bit_cast(v8, gw[ks]), dp[kb]);
             }
         }
-        // dS^T = P^T (dP^T - D), P^T = exp2(s*c - lse2), 0 for masked pairs
+        // dS^T = P^T (dP^T - D), P^T = exp2(s*c - lse2), 0 for masked pairs.
+        // Every exponential is formed (a row past the end has lse2 = +inf); the
+        // empty asm keeps each one out of a per-element branch, and the
+        // visibility test runs only on tiles that are not wholly visible.
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                bool vis = key < N && qi < N;
-                if (p.causal) vis = vis && key <= qi;
-                if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
-                const float pv = vis ? fast_exp2(fmaf(s[kb][j], c, -l2)) : 0.f;
-                s[kb][j] = pv * (dp[kb][j] - dsum);
+                s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2));
+                asm volatile("" : "+v"(s[kb][j]));
+            }
+        const bool all = !mrow && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
+        if (!all) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    bool vis = key < N && qi < N;
+                    if (p.causal) vis = vis && key <= qi;
+                    if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
+                    s[kb][j] = vis ? s[kb][j] : 0.f;
+                }
             }
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[kb][j] = s[kb][j] * (dp[kb][j] - dsum);
         // dQ^T += K^T dS^T, contraction over the tile's keys
 #pragma unroll
         for (int ks2 = 0; ks2 < KS; ++ks2) {
