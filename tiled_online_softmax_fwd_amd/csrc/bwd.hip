@@ -9,9 +9,10 @@
 // Three kernels, no atomics (bitwise deterministic):
 //   bwd_pre   D_i and lse_i * log2(e) per row (+inf for a row with no visible
 //             key, so that its P is exactly 0);
-//   bwd_dkdv  one workgroup per 32*NW keys (each wave owns 32 keys, whose K and
-//             V operands stay in registers), looping over 32-query tiles of Q
-//             and dO staged in LDS: S = Q K^T and dP = dO V^T put a key in each
+//   bwd_dkdv  one workgroup per 32*NW keys (each wave owns 32 keys; K^T in
+//             registers, V^T in LDS), looping over 64-query tiles of Q and dO
+//             staged in LDS (one barrier per tile, computed as two 32-row
+//             halves): S = Q K^T and dP = dO V^T put a key in each
 //             lane's column, which is the A-operand layout of dV += P^T dO and
 //             dK += dS^T Q (their dO and Q operands are transposing LDS reads);
 //   bwd_dq    one workgroup per 32*NW queries (Q and dO in registers; under
@@ -90,7 +91,7 @@ bwd_dkdv(BwdParams p)
 {
     using TR = H16<T>;
     using v8 = typename TR::v8;
-    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 32;
+    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 64, NH = BQ / 32;
     using Plan = TilePlan<BQ, CPR, NW, 0>;
     __shared__ u32x4 sq[2][BQ * CPR];
     __shared__ u32x4 sg[2][BQ * CPR];
@@ -175,66 +176,71 @@ bwd_dkdv(BwdParams p)
             if (threadIdx.x < BQ) row_terms(qt + 1);
         }
 
-        // causal: every query of the tile precedes every key of the wave, so
-        // the wave has nothing to add (it still took part in the copy above)
-        if (p.causal && q0 + BQ - 1 < k_wave) continue;
+        // the tile's two 32-row halves, one after the other
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int qh = q0 + 32 * h;
+            // causal: every query of the tile precedes every key of the wave, so
+            // the wave has nothing to add (it still took part in the copy above)
+            if (p.causal && qh + 31 < k_wave) continue;
 
-        // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
-        f32x16 s = (f32x16){};
+            // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
+            f32x16 s = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-            const u32x4 qa = sq[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
-            s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
-        }
-        // lse2 of the lane's 16 query rows: four 16-byte LDS reads
-        f32x4 l2v[4];
+            for (int ks = 0; ks < DK; ++ks) {
+                const u32x4 qa = sq[buf][(32 * h + col) * CPR + swz_k<CPR>(32 * h + col, ks * 2 + hh)];
+                s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
+            }
+            // lse2 of the lane's 16 query rows: four 16-byte LDS reads
+            f32x4 l2v[4];
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) l2v[g4] = *(const f32x4*)&s_l2[buf][8 * g4 + 4 * hh];
-        // P = exp2(s*c - lse2).  Every exponential is formed (rows past the end
-        // carry lse2 = +inf and give 0); the empty asm keeps each one out of a
-        // per-element branch.  Pairs that are not visible are then set to 0,
-        // on tiles that are not wholly visible only.
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            s[j] = fast_exp2(fmaf(s[j], c, -l2v[j >> 2][j & 3]));
-            asm volatile("" : "+v"(s[j]));
-        }
-        const bool all = keys_all_on && q0 + BQ <= N && (!p.causal || q0 >= k_wave + 31);
-        if (!all) {
+            for (int g4 = 0; g4 < 4; ++g4) l2v[g4] = *(const f32x4*)&s_l2[buf][32 * h + 8 * g4 + 4 * hh];
+            // P = exp2(s*c - lse2).  Every exponential is formed (rows past the end
+            // carry lse2 = +inf and give 0); the empty asm keeps each one out of a
+            // per-element branch.  Pairs that are not visible are then set to 0,
+            // on tiles that are not wholly visible only.
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int qi = q0 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                bool vis = key_on && qi < N;
-                if (p.causal) vis = vis && key <= qi;
-                s[j] = vis ? s[j] : 0.f;
+                s[j] = fast_exp2(fmaf(s[j], c, -l2v[j >> 2][j & 3]));
+                asm volatile("" : "+v"(s[j]));
             }
-        }
-        const v8 pa0 = pack8<T>(s, 0), pa1 = pack8<T>(s, 1);
-        // dV += P^T dO (contraction over the 32 queries)
+            const bool all = keys_all_on && qh + 32 <= N && (!p.causal || qh >= k_wave + 31);
+            if (!all) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            dv[db] = TR::mma32(pa0, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 0, db, lane)), dv[db]);
-            dv[db] = TR::mma32(pa1, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 1, db, lane)), dv[db]);
-        }
-        // dP = dO V^T, then dS = P (dP - D) in place
-        f32x16 dp = (f32x16){};
+                for (int j = 0; j < 16; ++j) {
+                    const int qi = qh + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    bool vis = key_on && qi < N;
+                    if (p.causal) vis = vis && key <= qi;
+                    s[j] = vis ? s[j] : 0.f;
+                }
+            }
+            const v8 pa0 = pack8<T>(s, 0), pa1 = pack8<T>(s, 1);
+            // dV += P^T dO (contraction over the half's 32 queries)
 #pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-            const u32x4 ga = sg[buf][col * CPR + swz_k<CPR>(col, ks * 2 + hh)];
-            dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][ks][lane]), dp);
-        }
-        // D of the same rows, read where it is used
-        f32x4 dsv[4];
+            for (int db = 0; db < DB; ++db) {
+                dv[db] = TR::mma32(pa0, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 2 * h, db, lane)), dv[db]);
+                dv[db] = TR::mma32(pa1, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 2 * h + 1, db, lane)), dv[db]);
+            }
+            // dP = dO V^T, then dS = P (dP - D) in place
+            f32x16 dp = (f32x16){};
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) dsv[g4] = *(const f32x4*)&s_d[buf][8 * g4 + 4 * hh];
+            for (int ks = 0; ks < DK; ++ks) {
+                const u32x4 ga = sg[buf][(32 * h + col) * CPR + swz_k<CPR>(32 * h + col, ks * 2 + hh)];
+                dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][ks][lane]), dp);
+            }
+            // D of the same rows, read where it is used
+            f32x4 dsv[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - dsv[j >> 2][j & 3]);
-        const v8 da0 = pack8<T>(dp, 0), da1 = pack8<T>(dp, 1);
-        // dK += dS^T Q
+            for (int g4 = 0; g4 < 4; ++g4) dsv[g4] = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            dk[db] = TR::mma32(da0, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 0, db, lane)), dk[db]);
-            dk[db] = TR::mma32(da1, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 1, db, lane)), dk[db]);
+            for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - dsv[j >> 2][j & 3]);
+            const v8 da0 = pack8<T>(dp, 0), da1 = pack8<T>(dp, 1);
+            // dK += dS^T Q
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dk[db] = TR::mma32(da0, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 2 * h, db, lane)), dk[db]);
+                dk[db] = TR::mma32(da1, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 2 * h + 1, db, lane)), dk[db]);
+            }
         }
     }
 
