@@ -166,3 +166,33 @@ def test_large_sampled_rows(attn):
                                   np.array([i]), False, (~vis).astype(np.uint8)[None, :])
         assert np.max(np.abs(o[0, bh, i] - ro[0])) <= gu.TOL_H16, f"row {r}"
         assert abs(l[0, bh, i] - rl[0]) <= gu.TOL_LSE_H16
+
+
+def test_degenerate_sizes(attn):
+    """One block covering everything (N <= block), N = 1, a block far larger
+    than N, and empty sizes: flags on give the dense result bitwise, flags off
+    give zeros and -inf, and B*H*N = 0 is a no-op."""
+    import torch
+    for N, block in ((1, 64), (50, 64), (64, 64), (65, 64), (200, 4096), (33, 32)):
+        p = synth.make_qkv(1, 2, N, 64, "bf16", 67)
+        q, k, v = gu.upload(p)
+        nb = (N + block - 1) // block
+        for causal in (False, True):
+            say("sparse degenerate", N, block, causal)
+            on = torch.ones((1, 2, nb, nb), dtype=torch.uint8, device="cuda")
+            o1, l1 = attn.fwd_sparse(q, k, v, on, block=block, causal=causal, br=128, bc=64)
+            o2, l2 = attn.fwd(q, k, v, causal=causal, br=128, bc=64)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), (N, block, causal)
+            off = torch.zeros_like(on)
+            o3, l3 = attn.fwd_sparse(q, k, v, off, block=block, causal=causal)
+            torch.cuda.synchronize()
+            assert bool((o3 == 0).all()) and bool(torch.isneginf(l3).all())
+    for shape in ((0, 2, 64, 64), (1, 0, 64, 64), (1, 2, 0, 64)):
+        say("sparse empty", shape)
+        z = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        nb = (shape[2] + 63) // 64
+        bm = torch.ones((shape[0], shape[1], nb, nb), dtype=torch.uint8, device="cuda")
+        o, l = attn.fwd_sparse(z, z, z, bm, block=64)
+        torch.cuda.synchronize()
+        assert o.shape == z.shape
