@@ -334,14 +334,17 @@ def attended_pairs(bm, N, block, causal):
     """Number of (row, key) pairs the block flags bm [B, H, nb, nb] switch on,
     after causality (counting only)."""
     nb = bm.shape[-1]
-    starts = np.arange(nb) * block
-    width = np.minimum(block, N - starts)                         # keys per key block
+    starts = np.arange(nb, dtype=np.int64) * block
+    width = np.minimum(block, N - starts)                         # rows (= keys) per block
+    full = width[:, None] * width[None, :]                        # [row block, key block]
     if causal:
-        i = np.arange(N)[:, None]
-        per_row = np.clip(i - starts[None, :] + 1, 0, width[None, :])   # [N, nb]
-        per_block = np.add.reduceat(per_row, starts, axis=0)            # [nb(row), nb(key)]
+        # blocks are square and aligned: below the diagonal every pair, above
+        # none, on it the r(r + 1)/2 pairs with key <= row
+        a = np.arange(nb)[:, None]
+        b = np.arange(nb)[None, :]
+        per_block = np.where(b < a, full, np.where(b == a, width[:, None] * (width[:, None] + 1) // 2, 0))
     else:
-        per_block = np.minimum(block, N - starts)[:, None] * width[None, :]
+        per_block = full
     return int((bm.astype(np.int64) * per_block[None, None]).sum())
 
 
