@@ -59,6 +59,23 @@ def traffic_record(workload_key):
     return rec
 
 
+def environment(torch, A):
+    """What a timing and a deviation depend on besides the inputs: the GPU and
+    the software versions (the tutorial's reproducibility checklist names GPU,
+    library versions, dtype, sizes and masking; the sizes and masking are in
+    the config)."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "rocm": rocm,
+            "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "libattn_version": int(A.lib().attn_version()), "dropout": None}
+
+
 def flops(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
@@ -259,6 +276,7 @@ def main():
     }
     if naive:
         line["naive_baseline"] = naive
+    line["env"] = environment(torch, A)
     print(json.dumps(line), flush=True)
 
 
@@ -327,6 +345,7 @@ def run_backward(args, torch, synth, A):
                      "kernel_ms_mean": float(kms.mean())},
         "cpu_baseline": cpu,
     }
+    line["env"] = environment(torch, A)
     print(json.dumps(line), flush=True)
 
 
@@ -423,6 +442,7 @@ def run_sparse(args, torch, synth, A):
                      "kernel_ms_mean": float(kms.mean())},
         "cpu_baseline": cpu,
     }
+    line["env"] = environment(torch, A)
     print(json.dumps(line), flush=True)
 
 
@@ -490,6 +510,7 @@ def run_decode(args, torch, synth, A):
                      "traffic": None, "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean())},
         "cpu_baseline": cpu,
     }
+    line["env"] = environment(torch, A)
     print(json.dumps(line), flush=True)
 
 
