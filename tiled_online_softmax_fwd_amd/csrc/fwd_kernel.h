@@ -488,6 +488,9 @@ fwd_m32_h16(FwdParams p)
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
         }
+        // causal: every key of the tile comes after every row of the wave, so
+        // the wave has nothing to add (it took part in the copy above)
+        if (p.causal && k0 > wave_q0 + 31) return;
 
         // S^T = K Q^T : 32 keys x 32 queries per block
         f32x16 s[NKB];
