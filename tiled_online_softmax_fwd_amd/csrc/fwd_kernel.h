@@ -509,10 +509,10 @@ fwd_m32_h16(FwdParams p)
 
         // masking -> -inf.  Accumulator element (kb, j) of this lane is key
         // k0 + 32*kb + 8*(j/4) + 4*hh + j%4.  The score products are issued
-        // inside each masking case, so that the masked scores stay in the
-        // registers the products wrote (one merge of the cases instead of a
-        // register copy of the tile after it; 3.5% faster at d = 64, bitwise
-        // the same result).
+        // inside each masking case, so that every case leaves its scores in
+        // the registers the products wrote: issued once before the cases, the
+        // compiler copied the whole tile to other registers where the cases
+        // join (3-6% slower at d = 64; the results are bitwise the same).
         const bool diag = p.causal && k0 + BC - 1 > wave_q0;
         const bool tail = k0 + BC > N;
         // block-sparse: some 32-key sub-block of the tile not attended by the
@@ -707,6 +707,9 @@ fwd_m32_f32(FwdParams p)
         stage_tile<BC, CPR, NT, 0>(sk, (const u32x4*)(K + (size_t)k0 * D), rows_valid, tid);
         stage_tile<BC, CPR, NT, 2>(sv, (const u32x4*)(V + (size_t)k0 * D), rows_valid, tid);
         __syncthreads();
+        // causal: every key of the tile comes after every row of the wave
+        // (the wave took part in the staging and both barriers)
+        if (p.causal && k0 > wave_q0 + 31) continue;
 
         f32x16 s[NKB];
 #pragma unroll
