@@ -382,7 +382,11 @@ struct BlockScan {
 // tiles whose state fits in 256 registers, one otherwise.
 template <int D, int BC> struct H16Occ { static constexpr int value = (D * BC <= 128 * 64) ? 2 : 1; };
 
-template <typename T, int D, int BR, int BC, bool SPARSE>
+// MASKED: the instance for calls with a key-padding mask (dense walk only).
+// Without one the padding test is compiled out; with one, the lane's padding
+// flags of the next key tile are loaded one tile ahead (32-bit words of four
+// flags), so that their latency hides behind a whole tile.
+template <typename T, int D, int BR, int BC, bool SPARSE, bool MASKED = false>
 __global__ void __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(H16Occ<D, BC>::value)))
 fwd_m32_h16(FwdParams p)
 {
@@ -460,6 +464,35 @@ fwd_m32_h16(FwdParams p)
 
     const int wave_q0 = q0 + wave * 32;
     const float c = p.c;
+
+    // padding flags (MASKED): word (kb, g4) holds the flags of keys
+    // k0 + 32*kb + 8*g4 + 4*hh + 0..3 in its four bytes; padw for the current
+    // tile, padn for the next one.  A word is one 32-bit load when the mask row
+    // is 4-byte aligned and the four keys lie inside the row, else four byte
+    // loads at clamped keys (flags of keys past N are never used).
+    static_assert(!(MASKED && SPARSE), "the block-sparse walk reads the mask in place");
+    const uint8_t* const prow = MASKED ? p.mask + (size_t)b * N : nullptr;
+    const bool pvec = MASKED && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[MASKED ? NKB : 1][4], padn[MASKED ? NKB : 1][4];
+    auto load_pad = [&](int k1) __attribute__((always_inline)) {
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int kbase = k1 + kb * 32 + 8 * g4 + 4 * hh;
+                    uint32_t w = 0;
+                    if (pvec && kbase + 3 < N) {
+                        w = *(const uint32_t*)(prow + kbase);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) w |= (uint32_t)prow[min(kbase + r, N - 1)] << (8 * r);
+                    }
+                    padn[kb][g4] = w;
+                }
+        }
+    };
+    if constexpr (MASKED) load_pad(tile_at(0) * BC);
     const int g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     typedef __attribute__((address_space(3))) char lds_char;
@@ -487,6 +520,15 @@ fwd_m32_h16(FwdParams p)
         } else if (it + 1 < kt_end) {
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
+        }
+        if constexpr (MASKED) {
+            // this tile's flags arrived with the wait above; fetch the next
+            // tile's
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) padw[kb][g4] = padn[kb][g4];
+            if (it + 1 < kt_end) load_pad(tile_at(it + 1) * BC);
         }
         // causal: every key of the tile comes after every row of the wave, so
         // the wave has nothing to add (it took part in the copy above)
@@ -521,8 +563,10 @@ fwd_m32_h16(FwdParams p)
         if (tail || p.mask || part) {
             scores();
             // ragged last tile, key padding or partly attended tile: full
-            // visibility test
-            const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
+            // visibility test (the MASKED instance has the padding flags in
+            // padw; the others read them in place, which only the block-sparse
+            // walk does: dense calls with a mask go to the MASKED instance)
+            const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * N : nullptr;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const bool on = !SPARSE || ((sub >> kb) & 1u);
@@ -530,6 +574,7 @@ fwd_m32_h16(FwdParams p)
                 for (int j = 0; j < 16; ++j) {
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
                     bool vis = on && key < N && (!p.causal || key <= qi);
+                    if constexpr (MASKED) vis = vis && ((padw[kb][j >> 2] >> (8 * (j & 3))) & 0xffu) == 0;
                     if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
                     if (!vis) s[kb][j] = -INFINITY;
                 }
@@ -805,7 +850,10 @@ template <typename T, int D, int BR, int BC, bool SPARSE = false>
 hipError_t launch_h16(const FwdParams& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
-    hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC, SPARSE>), dim3(grid), dim3(BR * 2), 0, st, p);
+    if (!SPARSE && p.mask)
+        hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC, false, true>), dim3(grid), dim3(BR * 2), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC, SPARSE, false>), dim3(grid), dim3(BR * 2), 0, st, p);
     return hipGetLastError();
 }
 
