@@ -521,6 +521,7 @@ fwd_m32_h16(FwdParams p)
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
         }
+        bool pad_any = false;     // MASKED: some key of the tile is padded
         if constexpr (MASKED) {
             // this tile's flags arrived with the wait above; fetch the next
             // tile's
@@ -529,6 +530,20 @@ fwd_m32_h16(FwdParams p)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) padw[kb][g4] = padn[kb][g4];
             if (it + 1 < kt_end) load_pad(tile_at(it + 1) * BC);
+            // the two wave halves hold all the tile's keys: a tile without a
+            // padded key takes the unmasked path, a tile with every key padded
+            // has nothing for this wave (flags past N repeat key N-1's)
+            uint32_t any = 0, zero = 0;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const uint32_t w = padw[kb][g4];
+                    any |= w;
+                    zero |= (w - 0x01010101u) & ~w & 0x80808080u;   // high bit of every zero byte
+                }
+            pad_any = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+            if (__builtin_amdgcn_ballot_w64(zero != 0) == 0) return;
         }
         // causal: every key of the tile comes after every row of the wave, so
         // the wave has nothing to add (it took part in the copy above)
@@ -560,7 +575,7 @@ fwd_m32_h16(FwdParams p)
         // block-sparse: some 32-key sub-block of the tile not attended by the
         // wave's rows (never with tiles no wider than a block)
         const bool part = SPARSE && sub != (1u << NKB) - 1u;
-        if (tail || p.mask || part) {
+        if (tail || (MASKED ? pad_any : p.mask != nullptr) || part) {
             scores();
             // ragged last tile, key padding or partly attended tile: full
             // visibility test (the MASKED instance has the padding flags in
