@@ -236,6 +236,29 @@ def test_tiles_16bit_causal_with_padding(attn, br, bc, dtype, d):
         assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scattered_padding_with_unaligned_mask_rows(attn, dtype, d, causal):
+    """Key padding with odd N (mask rows of odd batches are not 4-byte
+    aligned, so flags are read byte by byte there), scattered padded keys (key
+    tiles with and without a padded key), a fully padded sequence (its key
+    tiles are skipped) and a sequence whose first 200 keys are padded (its
+    first key tiles are wholly padded), at the default tiles in both orders."""
+    N = 301
+    p = synth.make_qkv(4, 2, N, d, dtype, 7)
+    rng = np.random.default_rng([7, N, 99])
+    mask = (rng.random((4, N)) < 0.01).astype(np.uint8)
+    mask[1, :] = 1
+    mask[2, :200] = 1
+    scale = float(np.float32(1 / math.sqrt(d)))
+    for order in (0, 1):
+        say("scattered padding", dtype, d, "causal", causal, "order", order)
+        e, o, l, ro, rl = check_full(attn, p, scale, causal, mask, f"{dtype} d{d} causal={causal} o{order}",
+                                     kv_order=order)
+        assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+
+
 # ------------------------------------------------------------------ edges
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
