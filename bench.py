@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
     ap.add_argument("--naive", action="store_true", help="also time the materialising baseline")
+    ap.add_argument("--padding", default="none", choices=["none", "c2"],
+                    help="key-padding mask of the forward: none, or c2 (batch 0 a random valid length, "
+                         "batch 1 fully padded, the rest unpadded)")
     ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "backward", "sparse"],
                     help="prefill: the causal forward (default); decode: Nq query rows against a key/value "
                          "cache; backward: gradient of the forward; sparse: block-sparse forward")
@@ -156,6 +159,8 @@ def main():
     print(f"[bench] generating inputs B{B} H{H} N{N} d{d} {args.dtype} causal={causal}", file=sys.stderr, flush=True)
     p = synth.make_qkv(B, H, N, d, args.dtype, 5)
     q, k, v = synth.upload(p)
+    pad = synth.c2_mask(B, N) if args.padding == "c2" else None
+    pad_t = torch.from_numpy(pad).cuda() if pad is not None else None
     out = torch.empty((B, H, N, d), dtype=q.dtype, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     br, bc = A.default_tiles({"bf16": A.BF16, "f16": A.F16, "f32": A.F32}[args.dtype], d, causal)
@@ -163,8 +168,8 @@ def main():
     bc = args.bc or bc
 
     def step():
-        A.fwd(q, k, v, scale=scale, causal=causal, out=out, lse=lse, br=br, bc=bc, kv_order=args.kv_order,
-              ref_slack=args.ref_slack)
+        A.fwd(q, k, v, scale=scale, causal=causal, key_padding_mask=pad_t, out=out, lse=lse, br=br, bc=bc,
+              kv_order=args.kv_order, ref_slack=args.ref_slack)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -225,7 +230,7 @@ def main():
         def time_rows(nr):
             rows = np.sort(rng.choice(B * H * N, size=nr, replace=False))
             t = time.perf_counter()
-            ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, causal)
+            ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, causal, pad)
             return time.perf_counter() - t, row_flops(rows), rows, ro, rl
 
         dt, f, rows, _, _ = time_rows(min(B * H * N, 256))
@@ -243,8 +248,14 @@ def main():
         check = {"rows": int(rows.size), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
                  "std_abs": float(err.std()), "lse_max_abs": float(np.abs(l_host[fin] - rl[fin]).max()),
                  "output": args.dtype}
+        if not fin.all():
+            # rows with no visible key: exactly (0, -inf) on both sides
+            check["empty_rows"] = int((~fin).sum())
+            check["empty_rows_exact"] = bool(np.all(np.isneginf(l_host[~fin])) and np.all(o_host[~fin] == 0))
 
     wk = f"B{B}_H{H}_N{N}_d{d}_{args.dtype}_{'causal' if causal else 'full'}_br{br}_bc{bc}"
+    if pad is not None:
+        wk += f"_pad{args.padding}"
     if args.ref_slack:
         wk += f"_slack{args.ref_slack}"
     tr = traffic_record(wk)
@@ -268,7 +279,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"B{B} H{H} N{N} d{d} {args.dtype} {'causal' if causal else 'non-causal'} attention forward",
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "br": br, "bc": bc,
-                   "kv_order": args.kv_order, "ref_slack": args.ref_slack, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+                   "kv_order": args.kv_order, "ref_slack": args.ref_slack, "key_padding": args.padding,
+                   "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
         "pct_peak": 100.0 * value / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
         "check_vs_fp64_oracle": check,
         "roofline": roof,
