@@ -83,6 +83,29 @@ def test_decode_padding_and_empty_rows(attn, dtype):
     assert np.all(o[:, :, :8] == 0) and np.all(np.isneginf(l[:, :, :8]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_scattered_padding_unaligned_rows(attn, d, causal):
+    """Key padding with an odd cache length (mask rows of odd batches are not
+    4-byte aligned, so flags are read byte by byte there), scattered padded
+    keys (tiles with and without a padded key), a fully padded cache (every
+    tile skipped) and a cache whose first 600 keys are padded (its first
+    tiles are wholly padded), with several query rows and key splits."""
+    B, H, Nq, Nk = 4, 2, 5, 1001
+    q, q64, k, k64, v, v64 = make(B, H, Nq, Nk, d, "bf16", 62)
+    rng = np.random.default_rng([62, Nk, 99])
+    mask = (rng.random((B, Nk)) < 0.01).astype(np.uint8)
+    mask[1, :] = 1
+    mask[2, :600] = 1
+    ro, rl = oracle.attn_kv(q64, k64, v64, 0.1, causal, mask)
+    for splits in (0, 3):
+        say("decode scattered padding", d, causal, splits)
+        o, l = run(attn, q, k, v, "bf16", 0.1, causal, mask, splits)
+        gu.assert_close(o, ro, gu.TOL_H16, f"decode scattered padding d{d} causal={causal} splits {splits}")
+        gu.assert_lse(l, rl, gu.TOL_LSE_H16, "decode scattered padding")
+        assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+
+
 def test_decode_empty_cache_and_sizes(attn):
     import torch
     q = torch.zeros((1, 2, 3, 64), dtype=torch.bfloat16, device="cuda")

@@ -27,7 +27,11 @@
 
 namespace attnk {
 
-template <typename T, int D>
+// MASKED: the instance for calls with a key-padding mask.  Each lane's padding
+// flags of the next key tile are loaded one tile ahead (a 32-bit word holds
+// the flags of four consecutive keys); a tile without a padded key skips the
+// padding test and a tile whose keys are all padded is skipped.
+template <typename T, int D, bool MASKED = false>
 __global__ void __launch_bounds__(64) dec_split(DecParams p)
 {
     constexpr int BC = 32;
@@ -60,7 +64,31 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
     if (p.causal) k_hi = min(k_hi, Nk - Nq + min(blockIdx.y * 16 + 15, Nq - 1) + 1);
     const int ntile = k_hi > k_lo ? (k_hi - k_lo + BC - 1) / BC : 0;
     const int last = p.causal ? Nk - Nq + qi : Nk - 1;   // last key this row sees
-    const uint8_t* mrow = p.mask ? p.mask + (size_t)b * Nk : nullptr;
+    const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * Nk : nullptr;
+    // MASKED: padw[kb] holds the flags of keys k0 + 16*kb + 4*g + 0..3 of the
+    // current tile, padn those of the next one; one 32-bit load when the mask
+    // row is 4-byte aligned and the keys lie inside the row, else four byte
+    // loads at clamped keys (flags past the cache end are never used)
+    const uint8_t* const prow = MASKED ? p.mask + (size_t)b * Nk : nullptr;
+    const bool pvec = MASKED && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[MASKED ? NKB : 1], padn[MASKED ? NKB : 1];
+    auto load_pad = [&](int k1) __attribute__((always_inline)) {
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int kbase = k1 + kb * 16 + 4 * g;
+                uint32_t w = 0;
+                if (pvec && kbase + 3 < Nk) {
+                    w = *(const uint32_t*)(prow + kbase);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) w |= (uint32_t)prow[min(kbase + r, Nk - 1)] << (8 * r);
+                }
+                padn[kb] = w;
+            }
+        }
+    };
+    if (MASKED && ntile > 0) load_pad(k_lo);
 
     KPlan kplan;
     VPlan vplan;
@@ -95,6 +123,21 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
             kplan.issue(sk[buf ^ 1], K, k0 + BC, Nk, 0);
             vplan.issue(sv[buf ^ 1], V, k0 + BC, Nk, 0);
         }
+        bool pad_any = false;
+        if constexpr (MASKED) {
+            // this tile's flags arrived with the wait above; fetch the next
+            // tile's.  The four lane groups hold all the tile's keys.
+            uint32_t any = 0, zero = 0;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                padw[kb] = padn[kb];
+                any |= padw[kb];
+                zero |= (padw[kb] - 0x01010101u) & ~padw[kb] & 0x80808080u;   // high bit of every zero byte
+            }
+            if (t + 1 < ntile) load_pad(k0 + BC);
+            pad_any = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+            if (__builtin_amdgcn_ballot_w64(zero != 0) == 0) continue;   // every key padded
+        }
 
         f32x4 s[NKB];
 #pragma unroll
@@ -115,6 +158,7 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
             for (int i = 0; i < 4; ++i) {
                 const int key = k0 + kb * 16 + 4 * g + i;
                 bool vis = key < k_hi && key <= last;
+                if constexpr (MASKED) vis = vis && (!pad_any || ((padw[kb] >> (8 * i)) & 0xffu) == 0);
                 if (mrow) vis = vis && mrow[min(key, Nk - 1)] == 0;
                 if (!vis) s[kb][i] = -INFINITY;
             }
@@ -209,7 +253,10 @@ template <typename T, int D>
 hipError_t launch_decode(const DecParams& p, hipStream_t st)
 {
     const unsigned qblocks = (unsigned)((p.Nq + 15) / 16);
-    hipLaunchKernelGGL((dec_split<T, D>), dim3((unsigned)(p.B * p.H * p.splits), qblocks), dim3(64), 0, st, p);
+    if (p.mask)
+        hipLaunchKernelGGL((dec_split<T, D, true>), dim3((unsigned)(p.B * p.H * p.splits), qblocks), dim3(64), 0, st, p);
+    else
+        hipLaunchKernelGGL((dec_split<T, D, false>), dim3((unsigned)(p.B * p.H * p.splits), qblocks), dim3(64), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((dec_merge<T, D>), dim3((unsigned)(p.B * p.H * p.Nq)), dim3(D), 0, st, p);
