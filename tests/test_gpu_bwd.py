@@ -80,6 +80,24 @@ def test_backward_padding(attn, dtype):
         assert np.all(x[1] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_scattered_padding_unaligned_rows(attn, d, causal):
+    """Key padding with odd N (mask rows of odd batches are not 4-byte
+    aligned), scattered padded keys (key tiles with and without a padded key),
+    a fully padded sequence and one whose first 200 keys are padded (wholly
+    padded key tiles, and waves whose keys are all padded)."""
+    B, N = 4, 301
+    rng = np.random.default_rng([71, N, 99])
+    mask = (rng.random((B, N)) < 0.01).astype(np.uint8)
+    mask[1, :] = 1
+    mask[2, :200] = 1
+    got, ref = run_bwd(attn, B, 2, N, d, "bf16", causal, mask, seed=71)
+    check(got, ref, f"bwd scattered padding d{d} causal {causal}")
+    for x in got:
+        assert np.all(x[1] == 0)
+
+
 def test_backward_sum_rule_and_determinism(attn):
     """sum_j dV_j = sum_i dO_i (rows of P sum to one) holds on the GPU, and two
     calls give bitwise-identical gradients."""

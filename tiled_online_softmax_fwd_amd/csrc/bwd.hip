@@ -85,7 +85,9 @@ __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
     return r;
 }
 
-template <typename T, int D, int NW>
+// MASKED (calls with a key-padding mask): a wave whose 32 keys are all padded
+// takes part in the copies and barriers only (its dK and dV stay zero).
+template <typename T, int D, int NW, bool MASKED = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 bwd_dkdv(BwdParams p)
 {
@@ -118,6 +120,7 @@ bwd_dkdv(BwdParams p)
     const int krow = min(key, N - 1);
     const bool key_on = key < N && !(p.mask && p.mask[(size_t)b * N + krow]);
     const bool keys_all_on = __builtin_amdgcn_ballot_w64(key_on) == ~0ull;   // wave-uniform
+    const bool keys_all_off = MASKED && __builtin_amdgcn_ballot_w64(key_on) == 0;
 
     // K^T and V^T operands of this lane's key: head columns 16*ks + 8*hh + 0..7.
     // K^T stays in registers; V^T goes to the wave's own LDS slots (each lane
@@ -176,6 +179,7 @@ bwd_dkdv(BwdParams p)
             if (threadIdx.x < BQ) row_terms(qt + 1);
         }
 
+        if (keys_all_off) continue;
         // the tile's two 32-row halves, one after the other
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
@@ -261,7 +265,11 @@ bwd_dkdv(BwdParams p)
     }
 }
 
-template <typename T, int D, int NW>
+// MASKED (calls with a key-padding mask): each lane's padding flags of the next
+// key tile are loaded one tile ahead (a 32-bit word holds the flags of four
+// consecutive keys); a tile without a padded key takes the unmasked path and
+// a tile whose keys are all padded is skipped.
+template <typename T, int D, int NW, bool MASKED = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 bwd_dq(BwdParams p)
 {
@@ -291,7 +299,32 @@ bwd_dq(BwdParams p)
     const int qrow = min(qi, N - 1);
     const float l2 = qi < N ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
     const float dsum = p.dsum[(size_t)bh * N + qrow];
-    const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
+    const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * N : nullptr;
+    // MASKED: padw[kb][g4] holds the flags of keys k0 + 32*kb + 8*g4 + 4*hh +
+    // 0..3 of the current tile, padn those of the next; one 32-bit load when
+    // the mask row is 4-byte aligned and the keys lie inside the row, else four
+    // byte loads at clamped keys (flags past N are never used)
+    const uint8_t* const prow = MASKED ? p.mask + (size_t)b * N : nullptr;
+    const bool pvec = MASKED && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[MASKED ? NKB : 1][4], padn[MASKED ? NKB : 1][4];
+    auto load_pad = [&](int k1) __attribute__((always_inline)) {
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int kbase = k1 + kb * 32 + 8 * g4 + 4 * hh;
+                    uint32_t w = 0;
+                    if (pvec && kbase + 3 < N) {
+                        w = *(const uint32_t*)(prow + kbase);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) w |= (uint32_t)prow[min(kbase + r, N - 1)] << (8 * r);
+                    }
+                    padn[kb][g4] = w;
+                }
+        }
+    };
 
     u32x4 qw[DK], gw[DK];
 #pragma unroll
@@ -314,6 +347,7 @@ bwd_dq(BwdParams p)
     if (kt_end > 0) {
         plan.issue(sk[0], K, 0, N, wave);
         plan.issue(sv[0], V, 0, N, wave);
+        if constexpr (MASKED) load_pad(0);
     }
     for (int kt = 0; kt < kt_end; ++kt) {
         const int buf = kt & 1;
@@ -323,6 +357,23 @@ bwd_dq(BwdParams p)
         if (kt + 1 < kt_end) {
             plan.issue(sk[buf ^ 1], K, k0 + BC, N, wave);
             plan.issue(sv[buf ^ 1], V, k0 + BC, N, wave);
+        }
+        bool pad_any = false;
+        if constexpr (MASKED) {
+            // this tile's flags arrived with the wait above; fetch the next
+            // tile's.  The two wave halves hold all the tile's keys.
+            uint32_t any = 0, zero = 0;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    padw[kb][g4] = padn[kb][g4];
+                    any |= padw[kb][g4];
+                    zero |= (padw[kb][g4] - 0x01010101u) & ~padw[kb][g4] & 0x80808080u;   // high bit of every zero byte
+                }
+            if (kt + 1 < kt_end) load_pad(k0 + BC);
+            pad_any = __builtin_amdgcn_ballot_w64(any != 0) != 0;
+            if (__builtin_amdgcn_ballot_w64(zero != 0) == 0) continue;   // every key padded
         }
         // causal: every key of the tile follows every query of the wave
         if (p.causal && k0 > wave_q0 + 31) continue;
@@ -354,7 +405,7 @@ bwd_dq(BwdParams p)
                 s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2));
                 asm volatile("" : "+v"(s[kb][j]));
             }
-        const bool all = !mrow && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
+        const bool all = !mrow && !pad_any && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
         if (!all) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -363,6 +414,7 @@ bwd_dq(BwdParams p)
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
                     bool vis = key < N && qi < N;
                     if (p.causal) vis = vis && key <= qi;
+                    if constexpr (MASKED) vis = vis && ((padw[kb][j >> 2] >> (8 * (j & 3))) & 0xffu) == 0;
                     if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
                     s[kb][j] = vis ? s[kb][j] : 0.f;
                 }
@@ -411,10 +463,13 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned tiles = (unsigned)((p.N + 32 * NW - 1) / (32 * NW));
-    hipLaunchKernelGGL((bwd_dkdv<T, D, NW>), dim3((unsigned)(p.B * p.H) * tiles), dim3(NW * 64), 0, st, p);
+    const dim3 grid((unsigned)(p.B * p.H) * tiles), block(NW * 64);
+    if (p.mask) hipLaunchKernelGGL((bwd_dkdv<T, D, NW, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((bwd_dkdv<T, D, NW, false>), grid, block, 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq<T, D, NW>), dim3((unsigned)(p.B * p.H) * tiles), dim3(NW * 64), 0, st, p);
+    if (p.mask) hipLaunchKernelGGL((bwd_dq<T, D, NW, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((bwd_dq<T, D, NW, false>), grid, block, 0, st, p);
     return hipGetLastError();
 }
 
