@@ -28,3 +28,19 @@ def test_block_mask_patterns():
     r2 = synth.block_mask(2, 3, 500, 32, 7, "random", 0.3)
     assert np.array_equal(r1, r2) and r1.shape == (2, 3, 16, 16)
     assert 0.2 < r1.mean() < 0.4
+
+
+def test_environment_record_keys():
+    """The env object of a bench line names the GPU, its architecture and the
+    software versions; checked with stand-ins for torch and the library."""
+    import types
+
+    props = types.SimpleNamespace(name="gpu-name", gcnArchName="gfx950:sramecc+:xnack-")
+    torch = types.SimpleNamespace(
+        __version__="9.9", version=types.SimpleNamespace(hip="7.0"),
+        cuda=types.SimpleNamespace(get_device_properties=lambda i: props))
+    A = types.SimpleNamespace(lib=lambda: types.SimpleNamespace(attn_version=lambda: 100))
+    env = bench.environment(torch, A)
+    assert env["gpu"] == "gpu-name" and env["arch"].startswith("gfx950")
+    assert env["hip_runtime"] == "7.0" and env["torch"] == "9.9" and env["libattn_version"] == 100
+    assert "rocm" in env and env["dropout"] is None
