@@ -260,7 +260,7 @@ struct TilePlan {
         for (int i = 0; i < NI; ++i) {
             const int p = (wave * NI + i) * 64 + lane;
             const int r = p / CPR, pc = p % CPR;
-            const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : swz_v16<CPR>(r, pc);
+            const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : (KIND == 1) ? swz_v16<CPR>(r, pc) : swz_v32(r, pc);
             row[i] = r;
             off[i] = (uint32_t)(r * CPR + c) * 16u;
         }
@@ -860,6 +860,179 @@ fwd_m32_f32(FwdParams p)
     }
 }
 
+// fp32 forward with the 16-bit kernel's staging: K and V tiles copied HBM ->
+// LDS by DMA into two buffers, the copy of tile t+1 in flight while tile t is
+// computed, one workgroup barrier per tile.  Used where two buffers of both
+// tiles fit in LDS; the arithmetic is that of fwd_m32_f32.
+template <int D, int BR, int BC>
+__global__ void __launch_bounds__(BR * 2)
+fwd_m32_f32_db(FwdParams p)
+{
+    constexpr int NW = BR / 32;
+    constexpr int CPR = D * 4 / 16;
+    constexpr int NKB = BC / 32, DB = D / 32, DH = D / 2, DC = D / 8;
+    using KPlan = TilePlan<BC, CPR, NW, 0>;
+    using VPlan = TilePlan<BC, CPR, NW, 2>;
+    static_assert(BR % 32 == 0 && BC % 32 == 0 && (D == 64 || D == 128), "tile");
+
+    __shared__ u32x4 sk[2][BC * CPR];
+    __shared__ u32x4 sv[2][BC * CPR];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int hh = lane >> 5, col = lane & 31;
+    int bh, qt;
+    tile_of_block(p, bh, qt);
+    const int N = p.N;
+    const int b = bh / p.H;
+    const int q0 = qt * BR;
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const float* __restrict__ Q = (const float*)p.q + head;
+    // the copy plans count rows in 2-byte units: one row is CPR * 8 of them
+    const uint16_t* __restrict__ K = (const uint16_t*)((const float*)p.k + head);
+    const uint16_t* __restrict__ V = (const uint16_t*)((const float*)p.v + head);
+    const int qi = q0 + wave * 32 + col;
+    const int wave_q0 = q0 + wave * 32;
+
+    const int nkt = (N + BC - 1) / BC;
+    int kt_end = nkt;
+    if (p.causal) kt_end = min(nkt, (min(q0 + BR, N) - 1) / BC + 1);
+    const int order = p.kv_order;
+    auto tile_at = [&](int it) { return order ? (kt_end - 1 - it) : it; };
+
+    KPlan kplan;
+    VPlan vplan;
+    kplan.init(wave, lane);
+    vplan.init(wave, lane);
+    kplan.issue(sk[0], K, tile_at(0) * BC, N, wave);
+    vplan.issue(sv[0], V, tile_at(0) * BC, N, wave);
+
+    // Q^T operand of 32x32x2: step t uses d = t + (D/2)*hh
+    float qf[DH];
+#pragma unroll
+    for (int t = 0; t < DC; ++t) {
+        f32x4 w = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (qi < N) w = *(const f32x4*)(Q + (size_t)qi * D + 4 * t + DH * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[4 * t + e] = w[e];
+    }
+
+    float m = -INFINITY, l = 0.f;
+    f32x16 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+    const float c = p.c;
+
+    auto body = [&](auto BUF, int it) __attribute__((always_inline)) {
+        constexpr int buf = decltype(BUF)::value;
+        const int k0 = tile_at(it) * BC;
+        // this tile landed; every wave is done with the previous one, so the
+        // other buffer can be refilled with the next tile
+        wait_vmcnt<0>();
+        wg_barrier();
+        if (it + 1 < kt_end) {
+            kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
+            vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
+        }
+        // causal: every key of the tile comes after every row of the wave
+        if (p.causal && k0 > wave_q0 + 31) return;
+
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = (f32x16){};
+            const int r = kb * 32 + col;
+#pragma unroll
+            for (int t = 0; t < DC; ++t) {
+                const f32x4 kv = __builtin_bit_cast(f32x4, sk[buf][r * CPR + swz_k<CPR>(r, t + DC * hh)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], qf[4 * t + e], s[kb], 0, 0, 0);
+            }
+        }
+
+        // invisible scores -> -inf; element (kb, j) is key k0 + 32*kb + 8*(j/4) + 4*hh + j%4.
+        // Rows of the ragged last tile past N hold row N-1's data (finite).
+        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                    bool vis = key < N;
+                    if (p.causal) vis = vis && key <= qi;
+                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    if (!vis) s[kb][j] = -INFINITY;
+                }
+            }
+        }
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mt = fmaxf(mt, s[kb][j]);
+        mt = xhalf_max(mt);
+        const RefStep rs = ref_step(m, mt, c, p.slack);
+        m = rs.m;
+        l *= rs.alpha;
+        if (__builtin_amdgcn_ballot_w64(rs.moved)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] *= rs.alpha;
+        }
+        const float mc = rs.mc;
+
+        const float* svf = (const float*)sv[buf];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -mc));
+                l += s[kb][j];
+            }
+            // O^T += V^T P^T, two keys per step: lane hh supplies key 8g+4hh+r
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = kb * 32 + 8 * g + 4 * hh + r;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const int dcol = db * 32 + col;
+                        const float a = svf[(row * CPR + swz_v32(row, dcol >> 2)) * 4 + (dcol & 3)];
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][4 * g + r], o[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    };
+    for (int it = 0; it < kt_end; it += 2) {
+        body(Int<0>{}, it);
+        if (it + 1 < kt_end) body(Int<1>{}, it + 1);
+    }
+
+    const float lt = xhalf_sum(l);
+    if (qi < N) {
+        const size_t orow = (size_t)bh * N + qi;
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = db * 32 + 8 * g4 + 4 * hh;
+                f32x4 x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = empty ? 0.f : o[db][4 * g4 + r] * inv;
+                *(f32x4*)((float*)p.o + orow * D + d0) = x;
+            }
+        }
+        if (p.lse && hh == 0)
+            p.lse[orow] = empty ? -INFINITY : fmaf(m, p.scale, __builtin_amdgcn_logf(lt) * 0.69314718055994530942f);
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename T, int D, int BR, int BC, bool SPARSE = false>
 hipError_t launch_h16(const FwdParams& p, hipStream_t st)
@@ -876,7 +1049,11 @@ template <int D, int BR, int BC>
 hipError_t launch_f32(const FwdParams& p, hipStream_t st)
 {
     const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
-    hipLaunchKernelGGL((fwd_m32_f32<D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
+    // two buffers of both tiles: 4 * BC rows of D fp32 values
+    if constexpr (4 * BC * D * 4 <= 128 * 1024)
+        hipLaunchKernelGGL((fwd_m32_f32_db<D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
+    else
+        hipLaunchKernelGGL((fwd_m32_f32<D, BR, BC>), dim3(grid), dim3(BR * 2), 0, st, p);
     return hipGetLastError();
 }
 
