@@ -236,7 +236,7 @@ def test_tiles_16bit_causal_with_padding(attn, br, bc, dtype, d):
         assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_scattered_padding_with_unaligned_mask_rows(attn, dtype, d, causal):
