@@ -262,7 +262,8 @@ def main():
     roof = {"bound": "mfma", "achieved": kernel_tflops, "peak": PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3,
             "unit": "TFLOP/s", "frac": kernel_tflops / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
             "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
-            "kernel": "fwd_m32_h16" if args.dtype != "f32" else "fwd_m32_f32",
+            "kernel": ("fwd_m32_h16" if args.dtype != "f32"
+                       else "fwd_m32_f32_db" if 4 * bc * d * 4 <= 128 * 1024 else "fwd_m32_f32"),
             "kernel_ms_mean": float(kms.mean())}
     line = {
         "metric": METRIC,
