@@ -97,11 +97,14 @@ def run_c3(A, torch):
 
 def run_c4(A, torch):
     d, H = 64, 8
-    res = {"workload": "B1 H8 d64 non-causal, default tiles", "rows": []}
+    tiles = {dt: A.default_tiles({"bf16": A.BF16_OUT_F32, "f32": A.F32}[dt], d, False) for dt in ("bf16", "f32")}
+    tile_txt = ", ".join(f"{dt} {br}x{bc}" for dt, (br, bc) in tiles.items())
+    res = {"workload": f"B1 H8 d64 non-causal, default tiles (Br x Bc: {tile_txt})", "rows": []}
     md = ["# Deviation from fp64 against sequence length (B1 H8 d64, non-causal)", "",
           "Command: `python -m tests.deviation_report --which c4` (repository root, one MI355X).", "",
           "Statistics of |delta| over all output elements; seeded inputs `default_rng([4, N, 0])`. "
-          "16-bit rows use fp32-stored outputs for both kernels.", "",
+          "16-bit rows use fp32-stored outputs for both kernels. "
+          f"Flash tiles (the defaults, Br x Bc): {tile_txt}.", "",
           "| dtype | N | flash vs fp64 max | mean | std | naive vs fp64 max | mean | std | flash vs naive max | mean | std |",
           "|---|---|---|---|---|---|---|---|---|---|---|"]
     for dtype in ("bf16", "f32"):
