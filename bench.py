@@ -264,7 +264,7 @@ def main():
             "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
             "kernel": ("fwd_m32_h16" if args.dtype != "f32"
                        else "fwd_m32_f32_db" if 4 * bc * d * 4 <= 128 * 1024 else "fwd_m32_f32"),
-            "kernel_ms_mean": float(kms.mean())}
+            "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())}
     line = {
         "metric": METRIC,
         "value": value,
@@ -355,7 +355,7 @@ def run_backward(args, torch, synth, A):
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "bwd_pre + bwd_dkdv + bwd_dq",
-                     "kernel_ms_mean": float(kms.mean())},
+                     "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
     line["env"] = environment(torch, A)
@@ -452,7 +452,7 @@ def run_sparse(args, torch, synth, A):
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "fwd_m32_h16 (block-sparse)",
-                     "kernel_ms_mean": float(kms.mean())},
+                     "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
     line["env"] = environment(torch, A)
@@ -520,7 +520,7 @@ def run_decode(args, torch, synth, A):
                    "Nk": Nk, "d": d, "causal": causal, "num_splits": args.splits, "workspace_bytes": int(need)},
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
-                     "traffic": None, "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean())},
+                     "traffic": None, "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
     line["env"] = environment(torch, A)
