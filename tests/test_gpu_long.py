@@ -110,3 +110,61 @@ def test_long_key_value_cache(attn):
     ro, rl = oracle.attn_kv(qp.q64, kv.k64, kv.v64, d ** -0.5, True)
     gu.assert_close(gu.host(o), ro, gu.TOL_H16, "long decode")
     gu.assert_lse(gu.host(l), rl, gu.TOL_LSE_H16, "long decode")
+
+
+def _big_head_problem(H, N, d, config_id):
+    """[1, H, N, d] bf16 q, k, v on the device with seeded data in heads 0 and
+    H - 1 and zeros elsewhere; returns the tensors and the two heads' problems."""
+    import torch
+    heads = {0: synth.make_qkv(1, 1, N, d, "bf16", config_id, 0),
+             H - 1: synth.make_qkv(1, 1, N, d, "bf16", config_id, 1)}
+    q, k, v = (torch.zeros((1, H, N, d), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    for h, p in heads.items():
+        hq, hk, hv = gu.upload(p)
+        q[0, h].copy_(hq[0, 0])
+        k[0, h].copy_(hk[0, 0])
+        v[0, h].copy_(hv[0, 0])
+    torch.cuda.synchronize()
+    return q, k, v, heads
+
+
+def test_forward_beyond_2_31_elements(attn):
+    """Each of q, k, v and o holds more than 2^31 elements (B1 H136 N131072
+    d128: 2.28e9, the last heads past 4 GiB of bf16 and 8 GiB of fp32 output).
+    Sampled rows of the first and last heads against the oracle: every element
+    and byte offset is formed in 64 bits."""
+    import torch
+    H, N, d = 136, 131072, 128
+    assert H * N * d > 2 ** 31 and (H - 1) * N * d * 2 >= 2 ** 32
+    say("forward beyond 2^31 elements", H, N, d)
+    q, k, v, heads = _big_head_problem(H, N, d, 72)
+    o, l = attn.fwd(q, k, v, scale=d ** -0.5, causal=True, out_fp32=True)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(1, 1, N, 10, 2)
+    for h, p in heads.items():
+        check_rows(gu.host(o[0, h][None, None]), gu.host(l[0, h][None, None]), p, rows, d ** -0.5, True,
+                   gu.TOL_H16, gu.TOL_LSE_H16, f"big head {h}")
+    # a head in between holds zeros: every score is 0, so o = mean of zero rows = 0
+    mid = gu.host(o[0, H // 2, ::4096])
+    assert np.all(mid == 0.0)
+    del q, k, v, o, l
+    torch.cuda.empty_cache()
+
+
+def test_decode_beyond_2_31_elements(attn):
+    """Key/value cache of more than 2^31 elements per tensor (B1 H136 Nk131072
+    d128), one query row per head; the first and last heads against the oracle."""
+    import torch
+    H, Nk, d = 136, 131072, 128
+    say("decode beyond 2^31 elements", H, Nk, d)
+    _, k, v, heads = _big_head_problem(H, Nk, d, 73)
+    qp = synth.make_qkv(1, H, 1, d, "bf16", 73, 2)
+    q = gu.upload(qp)[0]
+    o, l = attn.decode_fwd(q, k, v, scale=d ** -0.5, out_fp32=True)
+    torch.cuda.synchronize()
+    for h, p in heads.items():
+        ro, rl = oracle.attn_kv(qp.q64[:, h:h + 1], p.k64, p.v64, d ** -0.5)
+        gu.assert_close(gu.host(o[0, h]), ro[0, 0], gu.TOL_H16, f"decode big head {h}")
+        gu.assert_lse(gu.host(l[0, h]), rl[0, 0], gu.TOL_LSE_H16, f"decode big head {h}")
+    del q, k, v, o, l
+    torch.cuda.empty_cache()
