@@ -35,12 +35,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (MI355X spec)
 METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak; max|Δ| vs FP64 oracle"
-KERNEL_SOURCES = ["fwd_kernel.h"]      # source of the 16-bit forward kernel the bench times
+KERNEL_SOURCES = ["fwd_kernel.h"]      # default sources of a traffic record (the forward kernels)
 
 
-def kernel_hash():
+def kernel_hash(sources=None):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (sources or KERNEL_SOURCES):
         with open(os.path.join(ROOT, "tiled_online_softmax_fwd_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -54,7 +54,7 @@ def traffic_record(workload_key):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload_key)
-    if not rec or rec.get("kernel_hash") != kernel_hash():
+    if not rec or rec.get("kernel_hash") != kernel_hash(rec.get("sources")):
         return None
     return rec
 
@@ -498,6 +498,7 @@ def run_decode(args, torch, synth, A):
     esz = 2
     algo_bytes = B * H * (2 * Nk * d * esz + 2 * Nq * d * esz + 4 * Nq)     # K, V, Q, O, lse
     gbs = algo_bytes / (kms.mean() * 1e-3) / 1e9
+    tr = traffic_record(f"decode_B{B}_H{H}_Nq{Nq}_Nk{Nk}_d{d}_{args.dtype}_{'causal' if causal else 'full'}_s{args.splits}")
     print(f"[bench] decode {args.steps} steps: kernel mean {kms.mean() * 1e3:.1f} us, {gbs:.0f} GB/s", file=sys.stderr)
     check = cpu = None
     if not args.no_cpu:
@@ -520,7 +521,7 @@ def run_decode(args, torch, synth, A):
                    "Nk": Nk, "d": d, "causal": causal, "num_splits": args.splits, "workspace_bytes": int(need)},
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": 8000.0, "unit": "GB/s", "frac": gbs / 8000.0,
-                     "traffic": None, "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
+                     "traffic": (tr["hbm_bytes_per_launch"] if tr else None), "kernel": "dec_split + dec_merge", "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
     line["env"] = environment(torch, A)

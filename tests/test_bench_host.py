@@ -44,3 +44,46 @@ def test_environment_record_keys():
     assert env["gpu"] == "gpu-name" and env["arch"].startswith("gfx950")
     assert env["hip_runtime"] == "7.0" and env["torch"] == "9.9" and env["libattn_version"] == 100
     assert "rocm" in env and env["dropout"] is None
+
+
+def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
+    """A counter record is used only while the sources it names are unchanged;
+    records without a source list are tied to the forward kernel's source."""
+    import json
+
+    csrc = tmp_path / "tiled_online_softmax_fwd_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "fwd_kernel.h").write_text("forward v1")
+    (csrc / "decode.hip").write_text("decode v1")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    recs = {"fwd": {"kernel_hash": bench.kernel_hash(), "hbm_bytes_per_launch": 1.0},
+            "dec": {"kernel_hash": bench.kernel_hash(["decode.hip"]), "sources": ["decode.hip"],
+                    "hbm_bytes_per_launch": 2.0}}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(recs))
+    assert bench.traffic_record("fwd")["hbm_bytes_per_launch"] == 1.0
+    assert bench.traffic_record("dec")["hbm_bytes_per_launch"] == 2.0
+    assert bench.traffic_record("missing") is None
+    (csrc / "fwd_kernel.h").write_text("forward v2")
+    assert bench.traffic_record("fwd") is None
+    assert bench.traffic_record("dec")["hbm_bytes_per_launch"] == 2.0
+    (csrc / "decode.hip").write_text("decode v2")
+    assert bench.traffic_record("dec") is None
+
+
+def test_committed_traffic_records_are_complete():
+    """Every committed counter record carries what the bench and its summary
+    need: the kernel, both counters, both calibration factors and the bytes."""
+    import json
+    import os
+
+    with open(os.path.join(bench.ROOT, "profiles", "traffic.json")) as f:
+        recs = json.load(f)
+    assert recs
+    for key, r in recs.items():
+        for field in ("kernel", "kernel_hash", "fetch_kib", "write_kib", "fetch_scale", "write_scale",
+                      "hbm_bytes_per_launch", "summary"):
+            assert field in r, (key, field)
+        want = (r["fetch_kib"] * r["fetch_scale"] + r["write_kib"] * r["write_scale"]) * 1024
+        assert abs(r["hbm_bytes_per_launch"] - want) <= 1e-6 * want, key
+        assert os.path.exists(os.path.join(bench.ROOT, "profiles", r["summary"])), key
