@@ -141,16 +141,17 @@ int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
     return check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
 }
 
-// Key chunks of the decode path: about two one-wave workgroups per compute
-// unit (512 in all; measured on B8 H32 Nk 8192 and B1 H32 Nk 65536, longer
-// chunks stream better than more of them), whole 32-key tiles per chunk.
+// Key chunks of the decode path: about four one-wave workgroups per compute
+// unit (1024 in all), whole 32-key tiles per chunk.  Measured with the
+// non-temporal tile copies on B8 H32 Nk 8192 (Nq 1 and 16) and B1 H32 Nk 65536:
+// 1024 is best or within 2% of the best of 512 ... 8192 on all three.
 void decode_splits(int B, int H, int Nq, int Nk, int num_splits, int* splits, int* kps)
 {
     const int tiles = (Nk + 31) / 32;
     int s = num_splits;
     if (s <= 0) {
         const int64_t units = (int64_t)B * H * ((Nq + 15) / 16);
-        const int64_t want = units > 0 ? (512 + units - 1) / units : 1;
+        const int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
         s = (int)(want < 1024 ? want : 1024);
     }
     if (s > tiles) s = tiles;

@@ -37,8 +37,8 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
     constexpr int BC = 32;
     constexpr int CPR = D * 2 / 16;
     constexpr int NKB = BC / 16, DB = D / 16, NQ = D / 32;
-    using KPlan = TilePlan<BC, CPR, 1, 0>;
-    using VPlan = TilePlan<BC, CPR, 1, 1>;
+    using KPlan = TilePlan<BC, CPR, 1, 0, true>;   // K and V are read once: non-temporal
+    using VPlan = TilePlan<BC, CPR, 1, 1, true>;
     using v8 = typename M16<T>::v8;
     using v2 = typename Dot2<T>::v2;
     static_assert(D == 64 || D == 128, "head size");

@@ -224,16 +224,29 @@ __device__ __forceinline__ uint64_t uniform_ptr(const void* p)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// NT: the non-temporal cache policy, for data that is read exactly once (the
+// key/value cache of the decode path); tiles that other workgroups read again
+// from L2 (the forward) keep the default policy.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16(uint64_t gbase, uint32_t voff, uint32_t lds_base)
 {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\t"
-                 "s_mov_b32 m0, %3\n\t"
-                 "global_load_lds_dwordx4 %1, %2\n\t"
-                 "s_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %3\n\t"
+                     "global_load_lds_dwordx4 %1, %2 nt\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\t"
+                     "s_mov_b32 m0, %3\n\t"
+                     "global_load_lds_dwordx4 %1, %2\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(saved)
+                     : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_void*)p; }
@@ -246,7 +259,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // per tile only the uniform base pointer moves.  In the last tile rows past
 // the end are clamped to row N-1, so every load stays in bounds and padding
 // keys (masked to -inf) carry finite data.
-template <int BC, int CPR, int NW, int KIND>
+template <int BC, int CPR, int NW, int KIND, bool NT = false>
 struct TilePlan {
     static constexpr int CH = BC * CPR;
     static constexpr int NI = CH / (64 * NW);
@@ -273,12 +286,12 @@ struct TilePlan {
         const uint32_t lb = lds_addr(lds_tile);
         if (k0 + BC <= N) {
 #pragma unroll
-            for (int i = 0; i < NI; ++i) lds_dma16(gb, off[i], lb + (uint32_t)((wave * NI + i) * 64 * 16));
+            for (int i = 0; i < NI; ++i) lds_dma16<NT>(gb, off[i], lb + (uint32_t)((wave * NI + i) * 64 * 16));
         } else {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int over = max(k0 + row[i] - (N - 1), 0);     // rows past N-1 -> N-1
-                lds_dma16(gb, off[i] - (uint32_t)(over * CPR * 16), lb + (uint32_t)((wave * NI + i) * 64 * 16));
+                lds_dma16<NT>(gb, off[i] - (uint32_t)(over * CPR * 16), lb + (uint32_t)((wave * NI + i) * 64 * 16));
             }
         }
     }
