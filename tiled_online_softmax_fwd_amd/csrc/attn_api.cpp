@@ -141,17 +141,28 @@ int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
     return check_pointers(q, k, v, o, lse, B, H, N, d, dtype);
 }
 
-// Key chunks of the decode path: about four one-wave workgroups per compute
-// unit (1024 in all), whole 32-key tiles per chunk.  Measured with the
-// non-temporal tile copies on B8 H32 Nk 8192 (Nq 1 and 16) and B1 H32 Nk 65536:
-// 1024 is best or within 2% of the best of 512 ... 8192 on all three.
+// Key chunks of the decode path (whole 32-key tiles).  With units = B*H*ceil(Nq/16)
+// row blocks, the library aims at about 1024 one-wave workgroups but takes
+// fewer, down to about 512, where that keeps chunks at 1024 keys or more, and
+// never makes chunks shorter than 256 keys.  Measured with the non-temporal tile
+// copies (TB/s of the best split counts in brackets):
+//   B8 H32 Nk 8192, Nq 1 or 16, d 64 or 128: 4 chunks (1024 workgroups) [6.2-6.4];
+//   B1 H32 Nk 65536: 32 chunks (1024) [6.1]; B2 H8 Nk 32768: 32 chunks of 1024
+//   keys (512) [4.7, against 4.3 for 64 chunks]; B1 H8 Nk 16384: 64 chunks of 256
+//   keys (512) [2.0, against 1.3 for 16 chunks of 1024].
 void decode_splits(int B, int H, int Nq, int Nk, int num_splits, int* splits, int* kps)
 {
     const int tiles = (Nk + 31) / 32;
     int s = num_splits;
     if (s <= 0) {
         const int64_t units = (int64_t)B * H * ((Nq + 15) / 16);
-        const int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
+        const int64_t hi = units > 0 ? (1024 + units - 1) / units : 1;   // about 1024 workgroups
+        const int64_t lo = units > 0 ? (512 + units - 1) / units : 1;    // about 512 workgroups
+        const int64_t long_chunks = tiles / 32 > 1 ? tiles / 32 : 1;     // chunks of >= 1024 keys
+        const int64_t shortest = tiles / 8 > 1 ? tiles / 8 : 1;          // chunks of >= 256 keys
+        int64_t want = long_chunks > lo ? long_chunks : lo;
+        if (want > hi) want = hi;
+        if (want > shortest) want = shortest;
         s = (int)(want < 1024 ? want : 1024);
     }
     if (s > tiles) s = tiles;
