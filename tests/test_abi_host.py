@@ -156,3 +156,28 @@ def test_sparse_argument_checks():
     assert call(bmask=o + 64) == ALIAS
     assert call(d=96) == HEAD
     assert call(N=0, bmask=None) == OK          # empty problem: no-op before any pointer check
+
+
+def test_decode_default_chunking():
+    """The library's default key chunking, read back through the workspace size
+    (B*H*splits*Nq*(d+1) floats): about 1024 one-wave workgroups, fewer (down to
+    about 512) where that keeps chunks at 1024 keys or more, never chunks under
+    256 keys; an explicit count is kept, in whole 32-key tiles."""
+    L = A.lib()
+    L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+
+    def chunks(B, H, Nq, Nk, d, splits=0):
+        n = L.attn_decode_workspace_bytes(B, H, Nq, Nk, d, splits)
+        per = B * H * Nq * (d + 1) * 4
+        assert n % per == 0
+        return n // per
+    assert chunks(8, 32, 1, 8192, 128) == 4        # 1024 workgroups of 2048 keys
+    assert chunks(8, 32, 1, 8192, 64) == 4
+    assert chunks(8, 32, 16, 8192, 128) == 4
+    assert chunks(1, 32, 1, 65536, 128) == 32      # 1024 workgroups of 2048 keys
+    assert chunks(2, 8, 1, 32768, 128) == 32       # 512 workgroups of 1024 keys
+    assert chunks(1, 8, 1, 16384, 128) == 64       # 512 workgroups of 256 keys
+    assert chunks(1, 1, 1, 100, 64) == 1           # a short cache stays whole
+    assert chunks(8, 32, 1, 1001, 128) == 2
+    assert chunks(8, 32, 1, 8192, 128, 3) == 3     # an explicit count is taken as given
+    assert chunks(1, 2, 3, 100, 64, 3) == 2        # ... in whole 32-key tiles: 4 tiles give 2 chunks of 2
