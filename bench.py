@@ -180,6 +180,7 @@ def main():
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
@@ -187,6 +188,7 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    free1 = torch.cuda.mem_get_info()[0]
     kms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = wall * 1e3 / args.steps
     fl = flops(B, H, N, d, causal)
@@ -286,6 +288,10 @@ def main():
         "check_vs_fp64_oracle": check,
         "roofline": roof,
         "cpu_baseline": cpu,
+        # the library keeps no workspace: free device memory is unchanged over
+        # the timed calls, while the score matrix alone would have taken this
+        "memory": {"library_workspace_bytes": 0, "device_free_delta_bytes": int(free0 - free1),
+                   "score_matrix_bytes_if_stored": int(B * H * N * N * (4 if args.dtype == "f32" else 2))},
     }
     if naive:
         line["naive_baseline"] = naive
