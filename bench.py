@@ -71,9 +71,16 @@ def environment(torch, A):
             rocm = f.read().strip()
     except OSError:
         pass
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "rocm": rocm,
             "hip_runtime": torch.version.hip, "torch": torch.__version__,
-            "libattn_version": int(A.lib().attn_version()), "dropout": None}
+            "libattn_version": int(A.lib().attn_version()), "dropout": None,
+            "host_cpu": cpu, "host_threads": len(os.sched_getaffinity(0))}
 
 
 def flops(B, H, N, d, causal):

@@ -44,6 +44,7 @@ def test_environment_record_keys():
     assert env["gpu"] == "gpu-name" and env["arch"].startswith("gfx950")
     assert env["hip_runtime"] == "7.0" and env["torch"] == "9.9" and env["libattn_version"] == 100
     assert "rocm" in env and env["dropout"] is None
+    assert "host_cpu" in env and env["host_threads"] >= 1
 
 
 def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
