@@ -104,6 +104,8 @@ def main():
     ap.add_argument("--kv-order", type=int, default=0)
     ap.add_argument("--ref-slack", type=int, default=0,
                     help="lag allowed to the merge reference, base-2 units (0 = exact running maximum)")
+    ap.add_argument("--generic-loop", action="store_true",
+                    help="force the compiler-scheduled tile loop (no software-pipelined steady state)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-check", action="store_true", help="accepted for compatibility; the check is part of the cpu_baseline leg")
@@ -176,7 +178,7 @@ def main():
 
     def step():
         A.fwd(q, k, v, scale=scale, causal=causal, key_padding_mask=pad_t, out=out, lse=lse, br=br, bc=bc,
-              kv_order=args.kv_order, ref_slack=args.ref_slack)
+              kv_order=args.kv_order, ref_slack=args.ref_slack, generic_loop=args.generic_loop)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -267,6 +269,8 @@ def main():
         wk += f"_pad{args.padding}"
     if args.ref_slack:
         wk += f"_slack{args.ref_slack}"
+    if args.generic_loop:
+        wk += "_generic"
     tr = traffic_record(wk)
     roof = {"bound": "mfma", "achieved": kernel_tflops, "peak": PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3,
             "unit": "TFLOP/s", "frac": kernel_tflops / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
@@ -290,7 +294,7 @@ def main():
         "config": {"workload": f"B{B} H{H} N{N} d{d} {args.dtype} {'causal' if causal else 'non-causal'} attention forward",
                    "B": B, "H": H, "N": N, "d": d, "causal": causal, "br": br, "bc": bc,
                    "kv_order": args.kv_order, "ref_slack": args.ref_slack, "key_padding": args.padding,
-                   "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+                   "generic_loop": bool(args.generic_loop), "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
         "pct_peak": 100.0 * value / (PEAK_BF16_TFLOPS if args.dtype != "f32" else 157.3),
         "check_vs_fp64_oracle": check,
         "roofline": roof,

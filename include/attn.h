@@ -104,6 +104,13 @@ enum attn_status {
  *       modes the rounding of P no longer leaves the largest weight exact, which
  *       raises the deviation from the exact result (about 1.1x on N(0,1)
  *       inputs, 2x on strongly peaked rows) for a few percent of speed.
+ *   generic_loop: 0 (default) lets the 16-bit d = 128 kernel with 256 x 64
+ *       tiles run its key tiles that need no masking through the hand-
+ *       scheduled software pipeline (score products of the next tile beside
+ *       the softmax of the current one); non-zero forces the compiler-
+ *       scheduled tile loop everywhere.  Both do the same operations in the
+ *       same order per row, so their results are bitwise equal; the switch
+ *       exists to check exactly that.
  * The tile sizes and block order are the knobs the stability paper's
  * sequence-length and perturbation sweeps vary (its Figs. 5 and 6). */
 typedef struct attn_opts {
@@ -111,7 +118,8 @@ typedef struct attn_opts {
     int bc;
     int kv_order;
     int ref_slack;
-    int reserved[4];   /* must be zero */
+    int generic_loop;
+    int reserved[3];   /* must be zero */
 } attn_opts;
 
 /* Exact attention forward with the default tiles and ascending fold order. */

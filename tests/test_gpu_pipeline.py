@@ -1,0 +1,100 @@
+"""GPU: the software-pipelined steady state of the 16-bit d = 128 kernel (256 x
+64 tiles) against the compiler-scheduled tile loop of the same kernel
+(attn_opts.generic_loop = 1) and against the fp64 oracle.
+
+Both loops do the same per-row operations in the same order, so O and lse must
+be bitwise equal; the shapes below put the end of the pipelined range at every
+kind of boundary (no tile after it, a full tile, a ragged tile, the causal
+diagonal) and run the pipeline with zero, one and many iterations.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    import torch
+    assert torch.cuda.is_available()
+    import tiled_online_softmax_fwd_amd as A
+    A.lib()
+    return A
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def both(A, p, scale, causal, out_fp32):
+    import torch
+    q, k, v = gu.upload(p)
+    outs = []
+    for generic in (False, True):
+        o, l = A.fwd(q, k, v, scale=scale, causal=causal, out_fp32=out_fp32, generic_loop=generic)
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    return outs
+
+
+# N: 128 (two full tiles, nothing after), 150 / 130 (ragged tile right after the
+# range), 192 (full tile after), 200 (full then ragged), 512, 1000, 1024, 2112
+SHAPES = [(1, 2, 128), (1, 2, 130), (1, 2, 150), (2, 2, 192), (1, 3, 200), (2, 2, 512),
+          (1, 4, 1000), (2, 3, 1024), (1, 2, 2112)]
+
+
+@pytest.mark.parametrize("B,H,N", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_pipelined_equals_tile_loop_bitwise(attn, B, H, N, causal, dtype):
+    import torch
+    p = synth.make_qkv(B, H, N, 128, dtype, 70, variant=N)
+    scale = float(np.float32(128 ** -0.5))
+    for out_fp32 in (True, False):
+        say("pipeline vs tile loop", dtype, B, H, N, "causal", causal, "out_fp32", out_fp32)
+        (o1, l1), (o2, l2) = both(attn, p, scale, causal, out_fp32)
+        assert torch.equal(o1, o2), f"O differs: max {float((o1.double() - o2.double()).abs().max()):.3e}"
+        assert torch.equal(l1, l2), "lse differs"
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 2, 150), (2, 2, 512), (1, 4, 1000)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_pipelined_against_oracle(attn, B, H, N, causal):
+    import torch
+    p = synth.make_qkv(B, H, N, 128, "bf16", 71, variant=N)
+    scale = float(np.float32(128 ** -0.5))
+    say("pipeline vs oracle bf16", B, H, N, "causal", causal)
+    q, k, v = gu.upload(p)
+    o, l = attn.fwd(q, k, v, scale=scale, causal=causal, out_fp32=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn(p.q64, p.k64, p.v64, scale, causal)
+    gu.assert_close(gu.host(o), ro, gu.TOL_H16, "pipelined O")
+    gu.assert_lse(gu.host(l), rl, gu.TOL_LSE_H16, "pipelined lse")
+
+
+def test_pipelined_headline_shape_bitwise(attn):
+    """B1 H32 N8192 d128 bf16 causal, bf16 output: the benchmarked call."""
+    import torch
+    p = synth.make_qkv(1, 32, 8192, 128, "bf16", 5)
+    scale = float(np.float32(128 ** -0.5))
+    say("pipeline vs tile loop B1 H32 N8192 causal")
+    (o1, l1), (o2, l2) = both(attn, p, scale, True, False)
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+def test_pipelined_peaked_rows_bitwise(attn):
+    """Q and K x4 (score std about 16): the reference moves on few tiles, so
+    most iterations take the no-rescale branch of the pipeline."""
+    import torch
+    p = synth.make_qkv(2, 4, 1024, 128, "bf16", 72, qk_factor=4.0)
+    scale = float(np.float32(128 ** -0.5))
+    for causal in (False, True):
+        say("pipeline vs tile loop peaked rows causal", causal)
+        (o1, l1), (o2, l2) = both(attn, p, scale, causal, True)
+        assert torch.equal(o1, o2)
+        assert torch.equal(l1, l2)

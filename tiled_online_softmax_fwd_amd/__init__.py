@@ -30,7 +30,7 @@ class AttnError(RuntimeError):
 
 class attn_opts(ctypes.Structure):
     _fields_ = [("br", ctypes.c_int), ("bc", ctypes.c_int), ("kv_order", ctypes.c_int),
-                ("ref_slack", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
+                ("ref_slack", ctypes.c_int), ("generic_loop", ctypes.c_int), ("reserved", ctypes.c_int * 3)]
 
 
 _lib = None
@@ -77,9 +77,10 @@ def _raise(st):
         raise AttnError(st, lib().attn_last_error().decode())
 
 
-def make_opts(br=0, bc=0, kv_order=0, ref_slack=0):
+def make_opts(br=0, bc=0, kv_order=0, ref_slack=0, generic_loop=0):
     o = attn_opts()
     o.br, o.bc, o.kv_order, o.ref_slack = int(br or 0), int(bc or 0), int(kv_order or 0), int(ref_slack or 0)
+    o.generic_loop = int(bool(generic_loop))
     return o
 
 
@@ -133,14 +134,15 @@ def _prep(q, k, v, key_padding_mask, out, lse, out_f32, want_lse):
 
 
 def fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=None, lse=None,
-        out_fp32=False, br=None, bc=None, kv_order=0, ref_slack=0, want_lse=True, stream=None):
+        out_fp32=False, br=None, bc=None, kv_order=0, ref_slack=0, generic_loop=False, want_lse=True,
+        stream=None):
     """Exact attention forward through attn_fwd_ex.  Returns (out, lse)."""
     torch = _torch()
     B, H, N, d, code, out, lse, mask = _prep(q, k, v, key_padding_mask, out, lse, out_fp32, want_lse)
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
-    opts = make_opts(br, bc, kv_order, ref_slack)
+    opts = make_opts(br, bc, kv_order, ref_slack, generic_loop)
     st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                            int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s), ctypes.byref(opts))
     _raise(st)

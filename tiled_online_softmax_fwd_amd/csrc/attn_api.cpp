@@ -102,13 +102,16 @@ int check_pointers(const void* q, const void* k, const void* v, void* o, float* 
     return ATTN_OK;
 }
 
-int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, int* bc, int* order, int* slack)
+int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, int* bc, int* order, int* slack,
+                 int* generic = nullptr)
 {
     defaults(dtype, d, causal, br, bc);
     *order = 0;
     *slack = 0;
+    if (generic) *generic = 0;
     if (!opts) return ATTN_OK;
-    for (int i = 0; i < 4; ++i)
+    if (generic) *generic = opts->generic_loop != 0;
+    for (int i = 0; i < 3; ++i)
         if (opts->reserved[i] != 0) return fail(ATTN_ERR_TILE, "attn_opts.reserved[%d] must be 0", i);
     if (opts->br != 0) {
         if (!valid_br(opts->br)) return fail(ATTN_ERR_TILE, "br=%d not in {16,32,64,128,256}", opts->br);
@@ -129,11 +132,11 @@ int resolve_opts(int dtype, int d, int causal, const attn_opts* opts, int* br, i
 
 int check_all(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
-              const attn_opts* opts, int* br, int* bc, int* order, int* slack)
+              const attn_opts* opts, int* br, int* bc, int* order, int* slack, int* generic = nullptr)
 {
     int st = check_scalars(B, H, N, d, scale, dtype);
     if (st) return st;
-    st = resolve_opts(dtype, d, causal, opts, br, bc, order, slack);
+    st = resolve_opts(dtype, d, causal, opts, br, bc, order, slack, generic);
     if (st) return st;
     if (!find(dtype, d, *br, *bc))
         return fail(ATTN_ERR_TILE, "no kernel for dtype %d, d=%d, br=%d, bc=%d", dtype, d, *br, *bc);
@@ -197,8 +200,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 const uint8_t* key_padding_mask, int dtype, void* stream,
                 const attn_opts* opts)
 {
-    int br, bc, order, slack;
-    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order, &slack);
+    int br, bc, order, slack, generic;
+    const int st = check_all(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, opts, &br, &bc, &order, &slack,
+                             &generic);
     if (st) return st;
     if ((int64_t)B * H * N == 0) return ok();
 
@@ -211,6 +215,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.causal = causal ? 1 : 0;
     p.kv_order = order;
     p.slack = (float)slack;
+    p.pipe = generic ? 0 : 1;
     p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
     p.bmask = nullptr;
     p.blk = 0;
@@ -260,6 +265,7 @@ int attn_fwd_sparse(const void* q, const void* k, const void* v, void* o, float*
     p.causal = causal ? 1 : 0;
     p.kv_order = 0;
     p.slack = (float)slack;
+    p.pipe = 0;
     p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
     p.bmask = block_mask;
     p.blk = block;

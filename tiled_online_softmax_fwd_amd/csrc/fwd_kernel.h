@@ -29,6 +29,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "fwd_pipe_asm.h"
+
 namespace attnk {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -54,6 +58,7 @@ struct FwdParams {
     int kv_order;          // 0 ascending key tiles, 1 descending
     int out_f32;           // o is float instead of the input type
     float slack;           // lag allowed to the merge reference (base-2 units, 0 = exact maximum)
+    int pipe;              // 16-bit d = 128, 256 x 64: software-pipelined steady tiles (0 = tile loop only)
     const uint8_t* bmask;  // block-sparse kernels: [B][H][nb][nb] block flags, non-zero = attended
     int blk;               // block edge in rows (multiple of 32)
     int nb;                // ceil(N / blk)
@@ -676,6 +681,68 @@ fwd_m32_h16(FwdParams p)
         }
     };
 
+    // Steady state (16-bit, d = 128, 256 x 64, ascending order, exact
+    // reference): the key tiles that are full and need no mask for any row of
+    // the workgroup run through the software pipeline of fwd_pipe_asm.h (the
+    // score products of tile t+1 beside the softmax of tile t, then P.V of
+    // tile t beside the maximum of tile t+1).  It does this body's operations
+    // in this body's order per row.  It consumes the K/V copies issued above
+    // and leaves the next tile's copies in flight in the buffers the loop
+    // below expects (an even count of tiles), with m, l and o updated.
+    int it_first = 0;
+    if constexpr (!SPARSE && !MASKED && D == 128 && BR == 256 && BC == 64) {
+        int n_st = p.causal ? (q0 + 1) / BC : N / BC;
+        n_st = min(min(n_st, N / BC), kt_end) & ~1;
+        if (p.pipe && order == 0 && p.slack == 0.f && n_st >= 2) {
+            const uint32_t skb = lds_addr(sk[0]), svb = lds_addr(sv[0]);
+            uint32_t ka[8], va[4];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                ka[ks] = skb + (uint32_t)(col * 256 + (((ks * 2 + hh) ^ (col & 15)) * 16));
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                va[db] = svb + (uint32_t)((4 * hh + rsrc) * 256 + (((db * 4 + 2 * g + (qsrc >> 1)) ^ (rsrc << 2)) * 16) +
+                                          (qsrc & 1) * 8);
+            constexpr uint32_t TB = BC * CPR * 16;       // bytes of one K or V tile
+            uint32_t ko0 = kplan.off[0] + TB, ko1 = kplan.off[1] + TB;
+            uint32_t vo0 = vplan.off[0] + TB, vo1 = vplan.off[1] + TB;
+            const uint32_t kdst = __builtin_amdgcn_readfirstlane(skb + (uint32_t)(wave * 2 * 1024));
+            const uint32_t vdst = __builtin_amdgcn_readfirstlane(svb + (uint32_t)(wave * 2 * 1024));
+            const uint64_t kbase = uniform_ptr(K), vbase = uniform_ptr(V);
+            uint32_t pairs = __builtin_amdgcn_readfirstlane((uint32_t)(n_st - 2) / 2);
+            // the block copies the first tile after it (into buffer 0) only if
+            // that tile is full: it does not clamp rows to the head's end
+            const bool next_full = n_st < kt_end && (n_st + 1) * BC <= N;
+            const uint32_t has_next = __builtin_amdgcn_readfirstlane(next_full ? 1u : 0u);
+            uint64_t moved;
+            uint32_t m0save;
+            static_assert(KPlan::NI == 2 && VPlan::NI == 2, "pipeline copy plan");
+#define ATTN_PIPE_OPERANDS                                                                          \
+    : "+{v[0:15]}"(o[0]), "+{v[16:31]}"(o[1]), "+{v[32:47]}"(o[2]), "+{v[48:63]}"(o[3]),           \
+      "+{v224}"(m), "+{v225}"(l), "+{v220}"(ko0), "+{v221}"(ko1), "+{v222}"(vo0), "+{v223}"(vo1), \
+      [pairs] "+s"(pairs), [moved] "=&s"(moved), [m0save] "=&s"(m0save)                             \
+    : "{v[128:131]}"(qf[0]), "{v[132:135]}"(qf[1]), "{v[136:139]}"(qf[2]), "{v[140:143]}"(qf[3]),   \
+      "{v[144:147]}"(qf[4]), "{v[148:151]}"(qf[5]), "{v[152:155]}"(qf[6]), "{v[156:159]}"(qf[7]),   \
+      "{v208}"(ka[0]), "{v209}"(ka[1]), "{v210}"(ka[2]), "{v211}"(ka[3]), "{v212}"(ka[4]),          \
+      "{v213}"(ka[5]), "{v214}"(ka[6]), "{v215}"(ka[7]), "{v216}"(va[0]), "{v217}"(va[1]),          \
+      "{v218}"(va[2]), "{v219}"(va[3]), [c] "s"(c), [kbase] "s"(kbase), [vbase] "s"(vbase),         \
+      [kdst] "s"(kdst), [vdst] "s"(vdst), [has_next] "s"(has_next)                                  \
+    : ATTN_PIPE_CLOBBERS
+            if constexpr (std::is_same<T, __bf16>::value)
+                asm volatile(ATTN_PIPE_ASM_BF16 ATTN_PIPE_OPERANDS);
+            else
+                asm volatile(ATTN_PIPE_ASM_F16 ATTN_PIPE_OPERANDS);
+#undef ATTN_PIPE_OPERANDS
+            if (n_st < kt_end && !next_full) {
+                // ragged tile next: copied here with rows clamped to N - 1; the
+                // block's last barrier has released both buffers 0
+                kplan.issue(sk[0], K, n_st * BC, N, wave);
+                vplan.issue(sv[0], V, n_st * BC, N, wave);
+            }
+            it_first = n_st;
+        }
+    }
+
     if constexpr (SPARSE) {
         int t = t0;
         while (t < kt_end) {
@@ -688,7 +755,7 @@ fwd_m32_h16(FwdParams p)
             body(Int<1>{}, 0, t1 * BC, t < kt_end ? t * BC : -1, st1);
         }
     } else {
-        for (int it = 0; it < kt_end; it += 2) {
+        for (int it = it_first; it < kt_end; it += 2) {
             body(Int<0>{}, it, 0, 0, 0u);
             if (it + 1 < kt_end) body(Int<1>{}, it + 1, 0, 0, 0u);
         }
