@@ -98,3 +98,40 @@ def test_pipelined_peaked_rows_bitwise(attn):
         (o1, l1), (o2, l2) = both(attn, p, scale, causal, True)
         assert torch.equal(o1, o2)
         assert torch.equal(l1, l2)
+
+
+# Shapes whose work splits evenly over 256 compute units run on the persistent
+# grid (one workgroup per compute unit walking a list of query tiles, or of
+# causal pairs of query tiles); generic_loop = 1 runs one workgroup per query
+# tile.  (B, H, N, causal): one pair per workgroup; two and four pairs per
+# workgroup; query tiles without causal masking; a head count that is not a
+# multiple of 8 (no XCD affinity).
+PERSISTENT = [(1, 16, 8192, True), (1, 32, 4096, True), (2, 32, 8192, True), (2, 16, 4096, False),
+              (1, 4, 32768, True)]
+
+
+@pytest.mark.parametrize("B,H,N,causal", PERSISTENT)
+def test_persistent_grid_bitwise(attn, B, H, N, causal):
+    import torch
+    p = synth.make_qkv(B, H, N, 128, "bf16", 73, variant=N)
+    scale = float(np.float32(128 ** -0.5))
+    say("persistent grid vs one workgroup per tile", B, H, N, "causal", causal)
+    (o1, l1), (o2, l2) = both(attn, p, scale, causal, False)
+    assert torch.equal(o1, o2), f"O differs: max {float((o1.double() - o2.double()).abs().max()):.3e}"
+    assert torch.equal(l1, l2), "lse differs"
+
+
+def test_persistent_grid_sampled_rows_against_oracle(attn):
+    """B2 H32 N8192 causal (four causal pairs per workgroup): sampled rows
+    against the fp64 oracle."""
+    import torch
+    p = synth.make_qkv(2, 32, 8192, 128, "bf16", 74)
+    scale = float(np.float32(128 ** -0.5))
+    say("persistent grid B2 H32 N8192 causal vs oracle rows")
+    q, k, v = gu.upload(p)
+    o, l = attn.fwd(q, k, v, scale=scale, causal=True, out_fp32=True)
+    torch.cuda.synchronize()
+    rows = gu.sample_rows(2, 32, 8192, per_head=40, seed=75)
+    ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, True)
+    gu.assert_close(gu.host(o).reshape(-1, 128)[rows], ro, gu.TOL_H16, "persistent O rows")
+    gu.assert_lse(gu.host(l).reshape(-1)[rows], rl, gu.TOL_LSE_H16, "persistent lse rows")

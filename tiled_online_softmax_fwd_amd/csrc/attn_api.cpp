@@ -60,6 +60,40 @@ void defaults(int dtype, int d, int causal, int* br, int* bc)
     else { *br = 256; *bc = 64; }
 }
 
+// Compute units of the current device, queried once per device.
+int cu_count()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+    return n;
+}
+
+// Persistent grid of the 16-bit d = 128 forward with 256 x 64 tiles (the one
+// instance that has it): one workgroup per compute unit when the items (query
+// tiles, or causal pairs of query tiles of equal cost) split evenly over the
+// compute units; the items of a head then stay on one XCD when both the head
+// count and the grid are multiples of the 8 XCDs.  Otherwise one workgroup per
+// query tile (the hardware's dynamic dispatch balances uneven work better).
+void persistent_grid(attnk::FwdParams& p, int dtype, int d, int br, int bc)
+{
+    p.persist = 0;
+    p.xcd_affine = 0;
+    if (dtype == ATTN_F32 || d != 128 || br != 256 || bc != 64 || p.mask || !p.pipe || p.kv_order || p.slack != 0.f)
+        return;
+    const int G = cu_count();
+    const int64_t BH = (int64_t)p.B * p.H;
+    const int64_t iph = p.causal ? (p.n_qt + 1) / 2 : p.n_qt;
+    const int64_t items = BH * iph;
+    if (G <= 0 || items < G || items % G != 0) return;
+    p.persist = G;
+    p.xcd_affine = (BH % 8 == 0 && G % 8 == 0) ? 1 : 0;
+}
+
 attnk::LaunchFn find(int dtype, int d, int br, int bc)
 {
     switch (dtype) {
@@ -220,6 +254,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.bmask = nullptr;
     p.blk = 0;
     p.nb = 0;
+    persistent_grid(p, dtype, d, br, bc);
     const hipError_t e = find(dtype, d, br, bc)(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return ok();
@@ -266,6 +301,8 @@ int attn_fwd_sparse(const void* q, const void* k, const void* v, void* o, float*
     p.kv_order = 0;
     p.slack = (float)slack;
     p.pipe = 0;
+    p.persist = 0;
+    p.xcd_affine = 0;
     p.out_f32 = (dtype == ATTN_F16_OUT_F32 || dtype == ATTN_BF16_OUT_F32) ? 1 : 0;
     p.bmask = block_mask;
     p.blk = block;

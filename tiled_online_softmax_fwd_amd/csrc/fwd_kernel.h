@@ -59,6 +59,8 @@ struct FwdParams {
     int out_f32;           // o is float instead of the input type
     float slack;           // lag allowed to the merge reference (base-2 units, 0 = exact maximum)
     int pipe;              // 16-bit d = 128, 256 x 64: software-pipelined steady tiles (0 = tile loop only)
+    int persist;           // > 0: persistent grid of that many workgroups walking UnitSched's items
+    int xcd_affine;        // persistent items of head bh run on XCD bh % 8 (B*H and the grid multiples of 8)
     const uint8_t* bmask;  // block-sparse kernels: [B][H][nb][nb] block flags, non-zero = attended
     int blk;               // block edge in rows (multiple of 32)
     int nb;                // ceil(N / blk)
@@ -192,6 +194,54 @@ __device__ __forceinline__ void tile_of_block(const FwdParams& p, int& bh, int& 
     qt = lin / BH;
     if (p.causal) qt = p.n_qt - 1 - qt;
 }
+
+// Persistent schedule.  The grid holds one workgroup per compute unit and each
+// workgroup walks a list of items.  An item is one query tile, or under causal
+// masking the pair of query tiles (n_qt-1-r, r) of one head: its two tiles
+// cost the same number of key tiles for every r, so equal item counts give
+// equal work.  With xcd_affine, the items of head bh go to the workgroups of
+// XCD bh % 8 (workgroups are dealt to the 8 XCDs round-robin), so every head's
+// K and V are read through one XCD's L2, and the workgroups of a head sweep its
+// key tiles together (heaviest tile of each pair first).
+struct UnitSched {
+    int item, stride, n_items, iph, n_qt, causal, xcd, part;
+
+    __device__ __forceinline__ void init(const FwdParams& p)
+    {
+        n_qt = p.n_qt;
+        causal = p.causal;
+        iph = causal ? (n_qt + 1) / 2 : n_qt;
+        const int BH = p.B * p.H;
+        if (p.xcd_affine) {
+            xcd = (int)blockIdx.x & 7;
+            item = (int)blockIdx.x >> 3;
+            stride = p.persist >> 3;
+            n_items = (BH >> 3) * iph;
+        } else {
+            xcd = -1;
+            item = (int)blockIdx.x;
+            stride = p.persist;
+            n_items = BH * iph;
+        }
+        part = 0;
+    }
+    // the unit at the current position; false when the list is done
+    __device__ __forceinline__ bool get(int& bh, int& qt) const
+    {
+        if (item >= n_items) return false;
+        const int h = item / iph, r = item % iph;
+        bh = xcd >= 0 ? xcd + 8 * h : h;
+        qt = !causal ? r : (part == 0 ? n_qt - 1 - r : r);
+        return true;
+    }
+    __device__ __forceinline__ void advance()
+    {
+        const int r = item % iph;
+        if (causal && part == 0 && n_qt - 1 - r != r) { part = 1; return; }
+        part = 0;
+        item += stride;
+    }
+};
 
 // ============================================================ 16-bit, 32x32
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -426,8 +476,20 @@ fwd_m32_h16(FwdParams p)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const int hh = lane >> 5, col = lane & 31;
+    // Units: one per workgroup, or the items of a persistent schedule (this
+    // instance only).  A persistent workgroup copies the next unit's first K
+    // and V tiles while it stores the current unit's output.
+    constexpr bool PERSIST_OK = !SPARSE && !MASKED && D == 128 && BR == 256 && BC == 64;
+    UnitSched sched;
     int bh, qt;
-    tile_of_block(p, bh, qt);
+    if (PERSIST_OK && p.persist > 0) {
+        sched.init(p);
+        if (!sched.get(bh, qt)) return;
+    } else {
+        tile_of_block(p, bh, qt);
+    }
+    bool prefetched = false;
+    for (;;) {
     const int N = p.N;
     const int b = bh / p.H;
     const int q0 = qt * BR;
@@ -456,7 +518,7 @@ fwd_m32_h16(FwdParams p)
     VPlan vplan;
     kplan.init(wave, lane);
     vplan.init(wave, lane);
-    if (!SPARSE || t0 < kt_end) {
+    if ((!SPARSE || t0 < kt_end) && !prefetched) {
         kplan.issue(sk[0], K, t0 * BC, N, wave);
         vplan.issue(sv[0], V, t0 * BC, N, wave);
     }
@@ -513,7 +575,23 @@ fwd_m32_h16(FwdParams p)
     if constexpr (MASKED) load_pad(tile_at(0) * BC);
     const int g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    // Per-lane LDS byte addresses of the operand reads in buffer 0: K rows
+    // 32 kb + col at chunk 2 ks + hh, and the V^T pairs of rows 16 ks2 + 4 hh +
+    // rsrc (+ 8) at head column block db.  Both swizzles depend only on a row's
+    // position within its 16-row group, so the buffer, the key block kb and the
+    // key step ks2 only add constants.
+    constexpr uint32_t TILE_B = BC * CPR * 16;
+    uint32_t kaddr[DK], vaddr[DB];
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks)
+        kaddr[ks] = lds_addr(sk[0]) + (uint32_t)((col * CPR + swz_k<CPR>(col, ks * 2 + hh)) * 16);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int r = 4 * hh + rsrc;
+        vaddr[db] = lds_addr(sv[0]) +
+                    (uint32_t)((r * CPR + swz_v16<CPR>(r, db * 4 + 2 * g + (qsrc >> 1))) * 16 + (qsrc & 1) * 8);
+    }
 
     // One key tile: the it-th of the fold order (dense), or the tile starting
     // at key sk0 followed by the one at sk0next (-1: none) with the wave's
@@ -573,10 +651,10 @@ fwd_m32_h16(FwdParams p)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 s[kb] = (f32x16){};
-                const int r = kb * 32 + col;
 #pragma unroll
                 for (int ks = 0; ks < DK; ++ks) {
-                    const u32x4 kv = sk[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                    const u32x4 kv =
+                        *(const lds_u32x4*)(uintptr_t)(kaddr[ks] + buf * TILE_B + kb * (32 * CPR * 16));
                     s[kb] = TR::mma32(__builtin_bit_cast(v8, kv), qf[ks], s[kb]);
                 }
             }
@@ -662,18 +740,14 @@ fwd_m32_h16(FwdParams p)
         }
 
         // O^T += V^T P^T; V^T operand: keys 16*ks2 + {4*hh + r, 8 + 4*hh + r}, d = 32*db + col
-        lds_char* vbase = (lds_char*)sv[buf];
 #pragma unroll
         for (int ks2 = 0; ks2 < KS; ++ks2) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int chunk = db * 4 + 2 * g + (qsrc >> 1);
-                const int row1 = ks2 * 16 + 4 * hh + rsrc;
-                const int row2 = row1 + 8;
-                const int off1 = (row1 * CPR + swz_v16<CPR>(row1, chunk)) * 16 + (qsrc & 1) * 8;
-                const int off2 = (row2 * CPR + swz_v16<CPR>(row2, chunk)) * 16 + (qsrc & 1) * 8;
-                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off1));
-                const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + off2));
+                const uint32_t a1 = vaddr[db] + buf * TILE_B + ks2 * (16 * CPR * 16);
+                const uint32_t a2 = a1 + 8 * CPR * 16;
+                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+                const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a2);
                 const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
                 const u32x4 w = (u32x4){w1[0], w1[1], w2[0], w2[1]};
                 o[db] = TR::mma32(__builtin_bit_cast(v8, w), pb[ks2], o[db]);
@@ -695,14 +769,8 @@ fwd_m32_h16(FwdParams p)
         n_st = min(min(n_st, N / BC), kt_end) & ~1;
         if (p.pipe && order == 0 && p.slack == 0.f && n_st >= 2) {
             const uint32_t skb = lds_addr(sk[0]), svb = lds_addr(sv[0]);
-            uint32_t ka[8], va[4];
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                ka[ks] = skb + (uint32_t)(col * 256 + (((ks * 2 + hh) ^ (col & 15)) * 16));
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-                va[db] = svb + (uint32_t)((4 * hh + rsrc) * 256 + (((db * 4 + 2 * g + (qsrc >> 1)) ^ (rsrc << 2)) * 16) +
-                                          (qsrc & 1) * 8);
+            const uint32_t* ka = kaddr;
+            const uint32_t* va = vaddr;
             constexpr uint32_t TB = BC * CPR * 16;       // bytes of one K or V tile
             uint32_t ko0 = kplan.off[0] + TB, ko1 = kplan.off[1] + TB;
             uint32_t vo0 = vplan.off[0] + TB, vo1 = vplan.off[1] + TB;
@@ -717,22 +785,17 @@ fwd_m32_h16(FwdParams p)
             uint64_t moved;
             uint32_t m0save;
             static_assert(KPlan::NI == 2 && VPlan::NI == 2, "pipeline copy plan");
-#define ATTN_PIPE_OPERANDS                                                                          \
-    : "+{v[0:15]}"(o[0]), "+{v[16:31]}"(o[1]), "+{v[32:47]}"(o[2]), "+{v[48:63]}"(o[3]),           \
-      "+{v224}"(m), "+{v225}"(l), "+{v220}"(ko0), "+{v221}"(ko1), "+{v222}"(vo0), "+{v223}"(vo1), \
-      [pairs] "+s"(pairs), [moved] "=&s"(moved), [m0save] "=&s"(m0save)                             \
-    : "{v[128:131]}"(qf[0]), "{v[132:135]}"(qf[1]), "{v[136:139]}"(qf[2]), "{v[140:143]}"(qf[3]),   \
-      "{v[144:147]}"(qf[4]), "{v[148:151]}"(qf[5]), "{v[152:155]}"(qf[6]), "{v[156:159]}"(qf[7]),   \
-      "{v208}"(ka[0]), "{v209}"(ka[1]), "{v210}"(ka[2]), "{v211}"(ka[3]), "{v212}"(ka[4]),          \
-      "{v213}"(ka[5]), "{v214}"(ka[6]), "{v215}"(ka[7]), "{v216}"(va[0]), "{v217}"(va[1]),          \
-      "{v218}"(va[2]), "{v219}"(va[3]), [c] "s"(c), [kbase] "s"(kbase), [vbase] "s"(vbase),         \
-      [kdst] "s"(kdst), [vdst] "s"(vdst), [has_next] "s"(has_next)                                  \
-    : ATTN_PIPE_CLOBBERS
             if constexpr (std::is_same<T, __bf16>::value)
                 asm volatile(ATTN_PIPE_ASM_BF16 ATTN_PIPE_OPERANDS);
             else
                 asm volatile(ATTN_PIPE_ASM_F16 ATTN_PIPE_OPERANDS);
-#undef ATTN_PIPE_OPERANDS
+            // rebuild the copy plans instead of keeping them live across the
+            // block (the opaque wave copy stops the compiler from reusing the
+            // values computed before it)
+            int wv = wave;
+            asm volatile("" : "+s"(wv));
+            kplan.init(wv, lane);
+            vplan.init(wv, lane);
             if (n_st < kt_end && !next_full) {
                 // ragged tile next: copied here with rows clamped to N - 1; the
                 // block's last barrier has released both buffers 0
@@ -761,6 +824,24 @@ fwd_m32_h16(FwdParams p)
         }
     }
 
+    // persistent: the next unit's first K/V tiles are copied while this unit's
+    // output is normalised and stored (every wave is done with the LDS buffers
+    // after the barrier)
+    int nbh = 0, nqt = 0;
+    bool more = false;
+    if constexpr (PERSIST_OK) {
+        if (p.persist > 0) {
+            sched.advance();
+            more = sched.get(nbh, nqt);
+            if (more) {
+                const size_t nhead = (size_t)nbh * (size_t)N * D;
+                wg_barrier();
+                kplan.issue(sk[0], (const T*)p.k + nhead, 0, N, wave);
+                vplan.issue(sv[0], (const T*)p.v + nhead, 0, N, wave);
+            }
+        }
+    }
+
     // epilogue: O = acc / l, lse = m*scale + ln(l); empty rows -> (0, -inf)
     const float lt = xhalf_sum(l);
     if (qi < N) {
@@ -786,6 +867,11 @@ fwd_m32_h16(FwdParams p)
         if (p.lse && hh == 0)
             p.lse[orow] = empty ? -INFINITY : fmaf(m, p.scale, __builtin_amdgcn_logf(lt) * 0.69314718055994530942f);
     }
+    if (!more) break;
+    bh = nbh;
+    qt = nqt;
+    prefetched = true;
+    }   // units
 }
 
 // ============================================================ fp32, 32x32x2
@@ -1117,7 +1203,7 @@ fwd_m32_f32_db(FwdParams p)
 template <typename T, int D, int BR, int BC, bool SPARSE = false>
 hipError_t launch_h16(const FwdParams& p, hipStream_t st)
 {
-    const unsigned grid = (unsigned)(p.B * p.H * p.n_qt);
+    const unsigned grid = p.persist > 0 ? (unsigned)p.persist : (unsigned)(p.B * p.H * p.n_qt);
     if (!SPARSE && p.mask)
         hipLaunchKernelGGL((fwd_m32_h16<T, D, BR, BC, false, true>), dim3(grid), dim3(BR * 2), 0, st, p);
     else

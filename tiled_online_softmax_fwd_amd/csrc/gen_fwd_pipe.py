@@ -26,14 +26,15 @@ import sys
 O = 0            # v[0:63]    O^T accumulators, o[db] = v[16db : 16db+15]
 SA, SB = 64, 96  # v[64:127]  score tiles of two consecutive key tiles (P in place)
 Q = 128          # v[128:159] Q^T operand, qf[ks] = v[128+4ks : +3]
-KR, NKR = 160, 6     # v[160:183] ring of K operands (4 registers each)
-VR, NVR = 184, 6     # v[184:207] ring of V^T operands
-KADDR = 208      # v[208:215] LDS byte address of this lane's K chunk, per ks
-VADDR = 216      # v[216:219] LDS byte address of this lane's V^T pair, per db
-KOFF = 220       # v[220:221] byte offset of this lane's K copy chunks in the next K tile
-VOFF = 222       # v[222:223] the same for V
-M, L, NMC, ALPHA, MT, T0, T1 = 224, 225, 226, 227, 228, 229, 230
-NREG = 231       # v0 .. v230 are owned by the block
+NKR, NVR = 5, 5  # ring slots of K and V^T operands (4 registers each)
+KR = 160                     # K operand ring
+VR = KR + 4 * NKR            # V^T operand ring
+KADDR = VR + 4 * NVR         # 8: LDS byte address of this lane's K chunk, per ks
+VADDR = KADDR + 8            # 4: LDS byte address of this lane's V^T pair, per db
+KOFF = VADDR + 4             # 2: byte offset of this lane's K copy chunks in the next K tile
+VOFF = KOFF + 2              # 2: the same for V
+M, L, NMC, ALPHA, MT, T0, T1 = range(VOFF + 2, VOFF + 9)
+NREG = T1 + 1    # v0 .. v[NREG-1] are owned by the block
 # registers the loop writes with matrix or transcendental results (hazard
 # state assumed fresh for these where control flow joins)
 LOOP_WRITTEN = list(range(O, SB + 32)) + [M, L, NMC, ALPHA, MT, T0, T1]
@@ -417,7 +418,12 @@ class Gen:
 
     def iteration(self, cur, nxt, t_parity, k_dma, tag):
         """Iteration t: tile t's softmax and P.V, tile t+1's scores.
-        t_parity = t % 2.  k_dma: 'yes', 'no' or 'cond' (only if %[has_next])."""
+        t_parity = t % 2.  k_dma: 'yes', 'no' or 'cond' (only if %[has_next]).
+
+        Two complete versions follow the copies, chosen by whether any row of
+        the wave moved its reference on tile t: with the rescale of O (64
+        multiplies) in phase A, the first half of S(t+1)'s maximum and the copy
+        offset updates move to phase B to balance the two phases."""
         e = self.e
         kbn, vb = 1 - t_parity, t_parity
         self.barrier()
@@ -429,52 +435,49 @@ class Gen:
             self.dma("k", t_parity)
             e.label(f"{tag}5:")
         self.dma("v", 1 - t_parity)
+        offs = (KOFF,) if k_dma != "no" else ()
 
-        def phase_a_ops(rescale):
+        def version(rescale):
             a_pre = [self.lscale_op()] + self.chunk_ops(cur, 0, 0)[:16]
-            ops = self.chunk_ops(cur, 0, 0)[16:]
+            a_ops = self.chunk_ops(cur, 0, 0)[16:]
+            mx_a = self.max_ops(nxt, 0, True)
+            off_ops = self.offset_ops(offs) + self.offset_ops((VOFF,))
             if rescale:
-                ops += self.rescale_ops()
-            ops += self.offset_ops((KOFF,) if k_dma != "no" else ()) + self.offset_ops((VOFF,))
-            mx = self.max_ops(nxt, 0, True)
-            for o in mx:
-                o.lo = 11
-            c1 = self.chunk_ops(cur, 0, 1)[:16]      # fma + exp of chunk 1
-            return a_pre, ops + mx + c1
+                a_ops += self.rescale_ops()
+            else:
+                a_ops += off_ops
+                for o in mx_a:
+                    o.lo = 11
+                a_ops += mx_a
+            a_ops += self.chunk_ops(cur, 0, 1)[:16]      # fma + exp of chunk 1
+            vid = self.phase_s(nxt, kbn, a_ops, a_pre, vreads=(vb, 4))
+            # phase B: P chunk ks2 must be ready before the products of ks2
+            # (slot 4 ks2 - 1 is the last slot before them)
+            b_ops = self.chunk_ops(cur, 0, 1)[16:]      # conversion + sum of chunk 1
+            for o in b_ops:
+                o.hi = 2
+            if rescale:
+                b_ops += off_ops + mx_a
+            c2 = self.chunk_ops(cur, 1, 0)
+            for o in c2:
+                o.hi = 6
+            c3 = self.chunk_ops(cur, 1, 1)
+            for o in c3:
+                o.hi = 10
+            b_ops += self.max_ops(nxt, 1, False) + c2 + c3 + self.refstep_ops() + self.refstep_commit_ops()
+            self.phase_pv(cur, vb, b_ops, vid)
 
-        # phase A in two versions: with and without the rescale of O (no
-        # row of the wave moved its reference: alpha == 1 exactly)
         e.raw("s_cmp_eq_u64 %[moved], 0")
         e.raw(f"s_cbranch_scc1 {tag}1f")
         snap = e.snapshot()
-        pre, ops = phase_a_ops(True)
-        vid1 = self.phase_s(nxt, kbn, ops, pre, vreads=(vb, 4))
+        version(True)
         e.raw(f"s_branch {tag}2f")
         end1 = e.snapshot()
         e.label(f"{tag}1:")
         e.restore(snap)
-        pre, ops = phase_a_ops(False)
-        vid = self.phase_s(nxt, kbn, ops, pre, vreads=(vb, 4))
-        assert sorted(vid) == sorted(vid1)
-        # both paths leave the same V reads in flight, in the same order; the
-        # ids of the fall-through path stand for both
+        version(False)
         e.merge_with(end1)
         e.label(f"{tag}2:")
-        # phase B: P chunk ks2 must be ready before the products of ks2
-        # (slot 4 ks2 - 1 is the last slot before them)
-        c1 = self.chunk_ops(cur, 0, 1)[16:]         # conversion + sum of chunk 1
-        for o in c1:
-            o.hi = 2
-        c2 = self.chunk_ops(cur, 1, 0)
-        for o in c2:
-            o.hi = 6
-        c3 = self.chunk_ops(cur, 1, 1)
-        for o in c3:
-            o.hi = 10
-        mx = self.max_ops(nxt, 1, False)
-        rs = self.refstep_ops()
-        rc = self.refstep_commit_ops()
-        self.phase_pv(cur, vb, c1 + mx + c2 + c3 + rs + rc, vid)
 
     def prologue(self):
         """Tile 0: scores, maximum and reference step; K(1) copy issued."""
@@ -553,6 +556,19 @@ def main():
     for i in range(0, len(clob), 12):
         text += " \\\n    " + ", ".join(clob[i:i + 12]) + ("," if i + 12 < len(clob) else "")
     text += "\n"
+    v = lambda r: f'"{{v{r}}}"'
+    vr = lambda r, n: f'"{{v[{r}:{r + n - 1}]}}"'
+    outs = [f'"+{{v[{O + 16 * i}:{O + 16 * i + 15}]}}"(o[{i}])' for i in range(4)]
+    outs += [f'"+{{v{M}}}"(m)', f'"+{{v{L}}}"(l)', f'"+{{v{KOFF}}}"(ko0)', f'"+{{v{KOFF + 1}}}"(ko1)',
+             f'"+{{v{VOFF}}}"(vo0)', f'"+{{v{VOFF + 1}}}"(vo1)',
+             '[pairs] "+s"(pairs)', '[moved] "=&s"(moved)', '[m0save] "=&s"(m0save)']
+    ins = [f'{vr(Q + 4 * i, 4)}(qf[{i}])' for i in range(8)]
+    ins += [f'{v(KADDR + i)}(ka[{i}])' for i in range(8)] + [f'{v(VADDR + i)}(va[{i}])' for i in range(4)]
+    ins += ['[c] "s"(c)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)', '[vdst] "s"(vdst)',
+            '[has_next] "s"(has_next)']
+    text += ("\n// operands: fixed registers of the block bound to the kernel's variables\n"
+             "#define ATTN_PIPE_OPERANDS \\\n    : " + ", \\\n      ".join(outs) +
+             " \\\n    : " + ", \\\n      ".join(ins) + " \\\n    : ATTN_PIPE_CLOBBERS\n")
     for name, f16 in (("ATTN_PIPE_ASM_BF16", False), ("ATTN_PIPE_ASM_F16", True)):
         text += f"\n#define {name} \\\n" + render(f16).rstrip("\n").replace("\n", " \\\n") + "\n"
     path = os.path.join(here, "fwd_pipe_asm.h")
