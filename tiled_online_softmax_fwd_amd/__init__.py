@@ -110,26 +110,66 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check(t, name, device, dtypes, shape):
+    """Raise ValueError unless t lives on `device`, is contiguous, has one of
+    `dtypes` and exactly `shape`: the library writes through the raw pointer."""
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(x) for x in dtypes)}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    return t
+
+
+def _mask_arg(mask, name, device, shape):
+    """uint8/bool [B, N] padding mask on `device` (made contiguous), or None."""
+    if mask is None:
+        return None
+    torch = _torch()
+    if mask.device != device:
+        raise ValueError(f"{name} must be on {device}, got {mask.device}")
+    return _check(mask.contiguous(), name, device, (torch.uint8, torch.bool), shape)
+
+
+def _workspace(ws, need, device):
+    """Caller workspace on `device` (any dtype, contiguous) of at least `need`
+    bytes, or a new one; returns (tensor, size in bytes)."""
+    torch = _torch()
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=device)
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, {need} needed")
+    return ws, nbytes
+
+
 def _prep(q, k, v, key_padding_mask, out, lse, out_f32, want_lse):
     torch = _torch()
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must share one [B, H, N, d] shape")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous GPU tensors")
+    if not q.is_cuda:
+        raise ValueError("q, k, v must be GPU tensors")
+    dev = q.device
     B, H, N, d = q.shape
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, dev, (q.dtype,), (B, H, N, d))
     code = _dtype_code(q, out_f32)
     odt = torch.float32 if (out_f32 or q.dtype == torch.float32) else q.dtype
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=odt, device=q.device)
+        out = torch.empty((B, H, N, d), dtype=odt, device=dev)
+    _check(out, "out", dev, (odt,), (B, H, N, d))
     if lse is None and want_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if key_padding_mask is not None:
-        if key_padding_mask.dtype not in (torch.uint8, torch.bool) or tuple(key_padding_mask.shape) != (B, N):
-            raise ValueError("key_padding_mask must be a [B, N] uint8/bool tensor")
-        key_padding_mask = key_padding_mask.contiguous()
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", dev, (torch.float32,), (B, H, N))
+    key_padding_mask = _mask_arg(key_padding_mask, "key_padding_mask", dev, (B, N))
     return B, H, N, d, code, out, lse, key_padding_mask
 
 
@@ -157,11 +197,7 @@ def fwd_sparse(q, k, v, block_mask, *, block=64, scale=None, causal=False, key_p
     torch = _torch()
     B, H, N, d, code, out, lse, mask = _prep(q, k, v, key_padding_mask, out, lse, out_fp32, want_lse)
     nb = (N + int(block) - 1) // int(block) if block and int(block) > 0 else 0
-    if block_mask.dtype not in (torch.uint8, torch.bool) or tuple(block_mask.shape) != (B, H, nb, nb):
-        raise ValueError(f"block_mask must be a [B, H, {nb}, {nb}] uint8/bool tensor")
-    if not block_mask.is_cuda:
-        raise ValueError("block_mask must be a GPU tensor")
-    block_mask = block_mask.contiguous()
+    block_mask = _mask_arg(block_mask, "block_mask", q.device, (B, H, nb, nb))
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
@@ -181,12 +217,11 @@ def naive_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=N
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     need = lib().attn_naive_workspace_bytes(B, H, N, code)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().attn_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale),
                               int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s),
-                              _ptr(workspace), workspace.numel())
+                              _ptr(workspace), ws_bytes)
     _raise(st)
     return out, lse
 
@@ -200,31 +235,32 @@ def decode_fwd(q, k, v, *, scale=None, causal=False, key_padding_mask=None, out=
         raise ValueError("q [B,H,Nq,d] and k, v [B,H,Nk,d] do not match")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous GPU tensors")
+    if not q.is_cuda:
+        raise ValueError("q, k, v must be GPU tensors")
+    dev = q.device
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
+    _check(q, "q", dev, (q.dtype,), (B, H, Nq, d))
+    _check(k, "k", dev, (q.dtype,), (B, H, Nk, d))
+    _check(v, "v", dev, (q.dtype,), (B, H, Nk, d))
     code = _dtype_code(q, out_fp32)
     odt = torch.float32 if (out_fp32 or q.dtype == torch.float32) else q.dtype
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=odt, device=q.device)
+        out = torch.empty((B, H, Nq, d), dtype=odt, device=dev)
+    _check(out, "out", dev, (odt,), (B, H, Nq, d))
     if lse is None and want_lse:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    mask = key_padding_mask
-    if mask is not None:
-        if mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (B, Nk):
-            raise ValueError("key_padding_mask must be a [B, Nk] uint8/bool tensor")
-        mask = mask.contiguous()
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", dev, (torch.float32,), (B, H, Nq))
+    mask = _mask_arg(key_padding_mask, "key_padding_mask", dev, (B, Nk))
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     need = lib().attn_decode_workspace_bytes(B, H, Nq, Nk, d, int(num_splits))
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().attn_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                                int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s), _ptr(workspace),
-                               workspace.numel(), int(num_splits))
+                               ws_bytes, int(num_splits))
     _raise(st)
     return out, lse
 
@@ -233,30 +269,28 @@ def bwd(q, k, v, o, dout, lse, *, scale=None, causal=False, key_padding_mask=Non
     """Gradient of fwd w.r.t. q, k, v through attn_bwd (bf16 or f16 inputs; o and
     lse as returned by fwd with the same arguments).  Returns fp32 (dq, dk, dv)."""
     torch = _torch()
-    for t in (q, k, v, o, dout):
-        if not t.is_cuda or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError("q, k, v, o, dout must be contiguous GPU tensors of one shape and dtype")
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("the backward takes bf16 or fp16 tensors")
+    if q.dim() != 4 or not q.is_cuda:
+        raise ValueError("q must be a [B, H, N, d] GPU tensor")
+    dev = q.device
     B, H, N, d = q.shape
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, nm, dev, (q.dtype,), (B, H, N, d))
+    _check(lse, "lse", dev, (torch.float32,), (B, H, N))
     code = BF16 if q.dtype == torch.bfloat16 else F16
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
-    mask = key_padding_mask
-    if mask is not None:
-        if mask.dtype not in (torch.uint8, torch.bool) or tuple(mask.shape) != (B, N):
-            raise ValueError("key_padding_mask must be a [B, N] uint8/bool tensor")
-        mask = mask.contiguous()
+    mask = _mask_arg(key_padding_mask, "key_padding_mask", dev, (B, N))
     need = lib().attn_bwd_workspace_bytes(B, H, N)
-    if workspace is None:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     s = stream if stream is not None else torch.cuda.current_stream(q.device).cuda_stream
     st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         B, H, N, d, float(scale), int(bool(causal)), _ptr(mask), code, ctypes.c_void_p(s),
-                        _ptr(workspace), workspace.numel())
+                        _ptr(workspace), ws_bytes)
     _raise(st)
     return dq, dk, dv
 
