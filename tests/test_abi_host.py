@@ -87,8 +87,10 @@ def test_rejections():
     assert chk(ref_slack=-1) == TILE and chk(ref_slack=16) == TILE
     assert chk(ref_slack=8) == OK and chk(ref_slack=15) == OK
     assert chk(br=256, bc=128) == TILE and chk(br=256, dtype=A.F32) == TILE      # not compiled
-    for bad in (0.0, -0.125, float("inf"), float("nan")):
+    for bad in (float("inf"), float("-inf"), float("nan")):
         assert chk(scale=bad) == SCALE
+    for fine in (0.0, -0.0, -0.125, 1e-30, -3.0):     # every finite scale is accepted
+        assert chk(scale=fine) == OK
     assert chk(o=0x10000 + 16) == ALIAS                     # o inside q
     assert chk(lse=0x40000 + 64) == ALIAS                   # lse inside o
     assert A.lib().attn_last_error() != b""
@@ -121,7 +123,7 @@ def test_decode_argument_checks():
     # rejected before anything is launched (no GPU touched)
     assert dec(dtype=A.F32) == DTYPE
     assert dec(d=96) == HEAD
-    assert dec(scale=0.0) == SCALE
+    assert dec(scale=float("inf")) == SCALE and dec(scale=float("nan")) == SCALE
     assert dec(Nq=-1) == SHAPE
     assert dec(splits=1025) == TILE
     assert dec(q=None) == NULL

@@ -112,8 +112,19 @@ int check_scalars(int B, int H, int N, int d, float scale, int dtype)
     if ((int64_t)B * H * N >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_SHAPE, "B*H*N = %lld rows exceeds 2^31 - 1", (long long)B * H * N);
     if (d != 64 && d != 128) return fail(ATTN_ERR_HEAD_DIM, "head size d=%d, supported: 64, 128", d);
-    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_SCALE, "scale %g must be finite and > 0", (double)scale);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale %g must be finite", (double)scale);
     return ATTN_OK;
+}
+
+// Kernels that keep a running maximum of raw scores take a positive factor:
+// scale < 0 runs as |scale| on negated Q, scale = 0 as 1 on Q = 0 (q_mode16 in
+// fwd_kernel.h).  Returns the factor the kernels use and sets the Q mode.
+float kernel_scale(float scale, int* qmode)
+{
+    if (scale > 0.f) { *qmode = 0; return scale; }
+    if (scale < 0.f) { *qmode = 1; return -scale; }
+    *qmode = 2;
+    return 1.f;
 }
 
 int check_pointers(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -244,8 +255,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask;
     p.B = B; p.H = H; p.N = N;
     p.n_qt = (N + br - 1) / br;
-    p.scale = scale;
-    p.c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e), rounded once
+    p.scale = kernel_scale(scale, &p.qmode);
+    p.c = (float)((double)p.scale * 1.4426950408889634);   // scale * log2(e), rounded once
     p.causal = causal ? 1 : 0;
     p.kv_order = order;
     p.slack = (float)slack;
@@ -295,8 +306,8 @@ int attn_fwd_sparse(const void* q, const void* k, const void* v, void* o, float*
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.mask = key_padding_mask;
     p.B = B; p.H = H; p.N = N;
     p.n_qt = (N + br - 1) / br;
-    p.scale = scale;
-    p.c = (float)((double)scale * 1.4426950408889634);
+    p.scale = kernel_scale(scale, &p.qmode);
+    p.c = (float)((double)p.scale * 1.4426950408889634);
     p.causal = causal ? 1 : 0;
     p.kv_order = 0;
     p.slack = (float)slack;
@@ -384,7 +395,7 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
     const int64_t nmax = Nq > Nk ? Nq : Nk;
     if ((int64_t)B * H * nmax >= ((int64_t)1 << 31)) return fail(ATTN_ERR_SHAPE, "B*H*max(Nq, Nk) exceeds 2^31 - 1");
     if (d != 64 && d != 128) return fail(ATTN_ERR_HEAD_DIM, "head size d=%d, supported: 64, 128", d);
-    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_SCALE, "scale %g must be finite and > 0", (double)scale);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_SCALE, "scale %g must be finite", (double)scale);
     if (num_splits < 0 || num_splits > 1024) return fail(ATTN_ERR_TILE, "num_splits=%d not in 0..1024", num_splits);
     if ((int64_t)B * H * Nq == 0) return ok();
     if (!q || !o) return fail(ATTN_ERR_NULL, "q and o must be non-NULL");
@@ -417,8 +428,8 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
     p.part_lse = (float*)workspace + (size_t)B * H * splits * (size_t)Nq * d;
     p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk;
     p.splits = splits; p.keys_per_split = kps;
-    p.scale = scale;
-    p.c = (float)((double)scale * 1.4426950408889634);
+    p.scale = kernel_scale(scale, &p.qmode);
+    p.c = (float)((double)p.scale * 1.4426950408889634);
     p.slack = 0.f;
     p.causal = causal ? 1 : 0;
     p.out_f32 = elem_bytes_out(dtype) == 4 ? 1 : 0;
@@ -481,6 +492,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     p.dsum = (float*)workspace;
     p.lse2 = (float*)workspace + rows;
     p.B = B; p.H = H; p.N = N;
+    // the gradient forms P = exp(scale q.k - lse) and multiplies by scale at the
+    // end: any finite scale as given
     p.scale = scale;
     p.c = (float)((double)scale * 1.4426950408889634);
     p.causal = causal ? 1 : 0;

@@ -20,6 +20,7 @@ struct DecParams {
     float scale;            // natural-log factor of q.k
     float c;                // scale * log2(e)
     float slack;            // lag allowed to the merge reference (0 = exact maximum)
+    int qmode;              // non-positive scales, see q_mode16 in fwd_kernel.h
     int causal;             // query row i sees keys j <= Nk - Nq + i
     int out_f32;
 };

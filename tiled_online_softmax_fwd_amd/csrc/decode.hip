@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
     // Q^T operand: step ks contracts head columns 32*ks + 8*g + 0..7
     u32x4 qw[NQ];
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks) qw[ks] = *(const u32x4*)(Q + (size_t)qrow * D + 32 * ks + 8 * g);
+    for (int ks = 0; ks < NQ; ++ks) qw[ks] = q_mode16(*(const u32x4*)(Q + (size_t)qrow * D + 32 * ks + 8 * g), p.qmode);
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) asm volatile("" : "+v"(qw[ks]));
 

@@ -59,6 +59,7 @@ struct FwdParams {
     int out_f32;           // o is float instead of the input type
     float slack;           // lag allowed to the merge reference (base-2 units, 0 = exact maximum)
     int pipe;              // 16-bit d = 128, 256 x 64: software-pipelined steady tiles (0 = tile loop only)
+    int qmode;             // 0: Q as stored; 1: Q negated (scale < 0); 2: Q taken as 0 (scale = 0)
     int persist;           // > 0: persistent grid of that many workgroups walking UnitSched's items
     int xcd_affine;        // persistent items of head bh run on XCD bh % 8 (B*H and the grid multiples of 8)
     const uint8_t* bmask;  // block-sparse kernels: [B][H][nb][nb] block flags, non-zero = attended
@@ -89,6 +90,22 @@ __device__ __forceinline__ float xhalf_sum(float x)
     // both halves add (lower + upper) in the same order
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
+
+// Non-positive scales.  The merge keeps the running maximum of raw scores q.k
+// and applies the factor c > 0 in one fma, which presumes c > 0 (the pages'
+// factor is 1/sqrt(d)).  A negative scale is run as |scale| on scores negated
+// through Q (c (q.k) = |c| ((-q).k); a sign flip is exact and round-to-nearest
+// is symmetric, so the products are exactly negated), and a zero scale as
+// scale 1 on Q = 0 (every score 0: the softmax is uniform over the visible
+// keys, lse = ln(count)).  The host picks the mode; Q is transformed once, in
+// registers.
+__device__ __forceinline__ u32x4 q_mode16(u32x4 w, int qmode)
+{
+    if (qmode == 1) return w ^ 0x80008000u;          // sign bits of both 16-bit halves
+    if (qmode == 2) return (u32x4){0u, 0u, 0u, 0u};
+    return w;
+}
+__device__ __forceinline__ float q_mode32(float x, int qmode) { return qmode == 1 ? -x : (qmode == 2 ? 0.f : x); }
 
 // Reference of the online merge.  The merge multiplies l and acc by
 // exp(m_old - m_new) when the reference moves from m_old to m_new, and the
@@ -529,7 +546,7 @@ fwd_m32_h16(FwdParams p)
     u32x4 qw[DK];
     const int qrow = min(qi, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) qw[ks] = *(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8);
+    for (int ks = 0; ks < DK; ++ks) qw[ks] = q_mode16(*(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8), p.qmode);
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(qw[ks]));
     v8 qf[DK];
@@ -907,7 +924,7 @@ fwd_m32_f32(FwdParams p)
         f32x4 w = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (qi < N) w = *(const f32x4*)(Q + (size_t)qi * D + 4 * t + DH * hh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[4 * t + e] = w[e];
+        for (int e = 0; e < 4; ++e) qf[4 * t + e] = q_mode32(w[e], p.qmode);
     }
 
     float m = -INFINITY, l = 0.f;
@@ -1080,7 +1097,7 @@ fwd_m32_f32_db(FwdParams p)
         f32x4 w = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (qi < N) w = *(const f32x4*)(Q + (size_t)qi * D + 4 * t + DH * hh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qf[4 * t + e] = w[e];
+        for (int e = 0; e < 4; ++e) qf[4 * t + e] = q_mode32(w[e], p.qmode);
     }
 
     float m = -INFINITY, l = 0.f;

@@ -103,12 +103,12 @@ fwd_m16(FwdParams p)
         for (int u = 0; u < D / 16; ++u) {
             const f32x4 w = *(const f32x4*)((const float*)Q + (size_t)qrow * D + g * (D / 4) + 4 * u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qf[4 * u + e] = w[e];
+            for (int e = 0; e < 4; ++e) qf[4 * u + e] = q_mode32(w[e], p.qmode);
         }
     } else {
 #pragma unroll
         for (int ks = 0; ks < NQ; ++ks)
-            qf[ks] = __builtin_bit_cast(QV, *(const u32x4*)(Q + (size_t)qrow * D + 32 * ks + 8 * g));
+            qf[ks] = __builtin_bit_cast(QV, q_mode16(*(const u32x4*)(Q + (size_t)qrow * D + 32 * ks + 8 * g), p.qmode));
     }
 
     float m = -INFINITY, l = 0.f;
