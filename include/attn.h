@@ -38,7 +38,9 @@
  *   - key_padding_mask: DEVICE pointer to [B][N] bytes (non-zero = padded key,
  *     excluded from every query row of that batch), or NULL (no padding).
  *   - B, H, N >= 0 (any zero is a successful no-op), B*H*N < 2^31,
- *     d in {64, 128}; scale finite and > 0 (1/sqrt(d) in the usual use).
+ *     d in {64, 128}; scale any finite float (1/sqrt(d) in the usual use; a
+ *     negative scale is run as |scale| on negated q and scale 0 as a uniform
+ *     softmax over the visible keys, both exact).
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.  Every
  *     call is asynchronous on that stream; outputs are valid once the caller
  *     has synchronised it.  No entry point synchronises, allocates device
@@ -210,6 +212,7 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
 /* Workspace bytes attn_decode_fwd needs for these sizes and num_splits
  * (0 for invalid sizes). */
 size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
 
 /* Gradient of attn_fwd w.r.t. q, k and v (the tutorial asks to check outputs
  * and gradients).  Recomputes P tile by tile from the forward's lse:
