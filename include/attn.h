@@ -213,6 +213,24 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
  * (0 for invalid sizes). */
 size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 
+/* attn_decode_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same checks, kernels and results, with the partial results held in a
+ * fixed 16 MiB device array inside the library instead of a caller workspace.
+ * Each GPU the library runs on keeps its own copy until the process ends; the
+ * first call on a device looks its address up (hipGetSymbolAddress).  Nothing
+ * is allocated, by this call or later.
+ *   Limit: attn_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits) must not
+ *   exceed 16 MiB (16777216 bytes); larger calls return ATTN_ERR_WORKSPACE
+ *   before anything is launched.
+ *   Concurrency: every call on one GPU uses that GPU's array; calls that overlap
+ *   in time on one GPU (other streams, other threads) race and must not be
+ *   issued.  Every call writes each partial result it reads, so no state
+ *   carries over between calls.
+ * Other arguments, errors and stream semantics as attn_decode_fwd. */
+int attn_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            const uint8_t* key_padding_mask, int dtype, void* stream, int num_splits);
 
 /* Gradient of attn_fwd w.r.t. q, k and v (the tutorial asks to check outputs
  * and gradients).  Recomputes P tile by tile from the forward's lse:

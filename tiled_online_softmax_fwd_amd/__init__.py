@@ -17,7 +17,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HE
           4: "ATTN_ERR_DTYPE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_TILE", 7: "ATTN_ERR_SCALE",
           8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_sparse", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
-           "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes",
+           "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes", "attn_decode_fwd_noalloc",
            "attn_bwd", "attn_bwd_workspace_bytes",
            "attn_status_string", "attn_last_error", "attn_version")
 
@@ -55,6 +55,7 @@ def lib():
         L.attn_naive_workspace_bytes.argtypes = [i, i, i, i]
         L.attn_naive_workspace_bytes.restype = ctypes.c_size_t
         L.attn_decode_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t, i]
+        L.attn_decode_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, i, vp, i]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t]
@@ -66,7 +67,7 @@ def lib():
         L.attn_last_error.restype = ctypes.c_char_p
         L.attn_version.argtypes = []
         for fn in (L.attn_fwd, L.attn_fwd_ex, L.attn_fwd_sparse, L.attn_check_args, L.attn_default_tiles,
-                   L.attn_naive_fwd, L.attn_decode_fwd, L.attn_bwd, L.attn_version):
+                   L.attn_naive_fwd, L.attn_decode_fwd, L.attn_decode_fwd_noalloc, L.attn_bwd, L.attn_version):
             fn.restype = ctypes.c_int
         _lib = L
     return _lib

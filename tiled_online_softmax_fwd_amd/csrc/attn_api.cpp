@@ -439,6 +439,29 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
     return ok();
 }
 
+int attn_decode_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            const uint8_t* key_padding_mask, int dtype, void* stream, int num_splits)
+{
+    // Same checks and kernels as attn_decode_fwd; the partial results go to the
+    // library's fixed device array instead of a caller workspace.  Every host
+    // check runs first: without a workspace attn_decode_fwd stops at
+    // ATTN_ERR_WORKSPACE only when every other argument is valid (and returns
+    // ATTN_OK for empty sizes), before any HIP call.
+    const int st = attn_decode_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, key_padding_mask, dtype,
+                                   stream, nullptr, 0, num_splits);
+    if (st != ATTN_ERR_WORKSPACE) return st;
+    const size_t need = attn_decode_workspace_bytes(B, H, Nq, Nk, d, num_splits);
+    if (need > attnk::DECODE_SCRATCH_BYTES)
+        return fail(ATTN_ERR_WORKSPACE, "decode without allocation: %zu bytes of partial results exceed the "
+                    "library's %zu-byte scratch (fewer rows or key splits needed)", need, attnk::DECODE_SCRATCH_BYTES);
+    void* ws = nullptr;
+    const hipError_t e = attnk::decode_scratch(&ws);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode scratch lookup: %s", hipGetErrorString(e));
+    return attn_decode_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, key_padding_mask, dtype, stream,
+                           ws, attnk::DECODE_SCRATCH_BYTES, num_splits);
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N)
 {
     if (B <= 0 || H <= 0 || N <= 0) return 0;

@@ -30,4 +30,13 @@ typedef hipError_t (*DecLaunchFn)(const DecParams&, hipStream_t);
 // dtype_bits: 0 bf16, 1 f16; D in {64, 128}; nullptr otherwise
 DecLaunchFn lookup_decode(int dtype_bits, int D);
 
+// Device scratch of attn_decode_fwd_noalloc: the same partial outputs and lse
+// the caller's workspace holds for attn_decode_fwd, in a fixed array of this
+// many bytes that each GPU keeps until the process ends.
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)16 << 20;
+
+// Device address of the scratch array on the current device (looked up with
+// hipGetSymbolAddress on the first call on each device, then cached).
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace attnk

@@ -263,6 +263,30 @@ hipError_t launch_decode(const DecParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
+// The scratch of attn_decode_fwd_noalloc.  Host code never uses this name as
+// an address (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[DECODE_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void** ptr)
+{
+    constexpr int MAX_DEV = 64;
+    static void* addr[MAX_DEV];          // per device; a racing first lookup stores the same value
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 DecLaunchFn lookup_decode(int dtype_bits, int D)
 {
     // dtype_bits: 0 bf16, 1 f16
