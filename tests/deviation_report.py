@@ -13,7 +13,7 @@ mean and std of |delta| and the mean of the signed delta.
   c3: B2 H16 N4096 d128 bf16, Q and K scaled by 4, non-causal; every
       (Br, Bc) in {16, 32, 64, 128}^2, both key-tile orders; plus the naive GPU
       baseline.
-  c4: B1 H8 d64, N in {512, ..., 16384}, bf16 and fp32, non-causal, default
+  c4: B1 H8 d64, N in {512, ..., 16384}, bf16, fp16 and fp32, non-causal, default
       tiles; flash vs fp64, naive vs fp64, flash vs naive.
 
 The 16-bit rows use the fp32-output flavour (same kernel, fp32 store) so the
@@ -97,7 +97,8 @@ def run_c3(A, torch):
 
 def run_c4(A, torch):
     d, H = 64, 8
-    tiles = {dt: A.default_tiles({"bf16": A.BF16_OUT_F32, "f32": A.F32}[dt], d, False) for dt in ("bf16", "f32")}
+    tiles = {dt: A.default_tiles({"bf16": A.BF16_OUT_F32, "f16": A.F16_OUT_F32, "f32": A.F32}[dt], d, False)
+             for dt in ("bf16", "f16", "f32")}
     tile_txt = ", ".join(f"{dt} {br}x{bc}" for dt, (br, bc) in tiles.items())
     res = {"workload": f"B1 H8 d64 non-causal, default tiles (Br x Bc: {tile_txt})", "rows": []}
     md = ["# Deviation from fp64 against sequence length (B1 H8 d64, non-causal)", "",
@@ -107,7 +108,7 @@ def run_c4(A, torch):
           f"Flash tiles (the defaults, Br x Bc): {tile_txt}.", "",
           "| dtype | N | flash vs fp64 max | mean | std | naive vs fp64 max | mean | std | flash vs naive max | mean | std |",
           "|---|---|---|---|---|---|---|---|---|---|---|"]
-    for dtype in ("bf16", "f32"):
+    for dtype in ("bf16", "f16", "f32"):
         for N in (512, 1024, 2048, 4096, 8192, 16384):
             p = synth.make_qkv(1, H, N, d, dtype, 4)
             say("c4 oracle", dtype, N)

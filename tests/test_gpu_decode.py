@@ -21,6 +21,11 @@ def attn():
     return A
 
 
+# fp32(0.1): the library receives the scale as a float and the oracle widens
+# the same value
+S01 = float(np.float32(0.1))
+
+
 def say(*a):
     print("[case]", *a, flush=True)
 
@@ -67,17 +72,17 @@ def test_decode_padding_and_empty_rows(attn, dtype):
     B, H, Nq, Nk, d = 4, 2, 8, 700, 128
     q, q64, k, k64, v, v64 = make(B, H, Nq, Nk, d, dtype, 60)
     mask = synth.c2_mask(B, Nk)
-    ro, rl = oracle.attn_kv(q64, k64, v64, 0.1, False, mask)
+    ro, rl = oracle.attn_kv(q64, k64, v64, S01, False, mask)
     for splits in (0, 3):
         say("decode padding", dtype, splits)
-        o, l = run(attn, q, k, v, dtype, 0.1, False, mask, splits)
+        o, l = run(attn, q, k, v, dtype, S01, False, mask, splits)
         gu.assert_close(o, ro, gu.TOL_H16, "decode padding")
         gu.assert_lse(l, rl, gu.TOL_LSE_H16, "decode padding")
         assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
     q, q64, k, k64, v, v64 = make(1, 2, 20, 12, 64, dtype, 61)
-    ro, rl = oracle.attn_kv(q64, k64, v64, 0.1, True)
+    ro, rl = oracle.attn_kv(q64, k64, v64, S01, True)
     say("decode Nq > Nk causal", dtype)
-    o, l = run(attn, q, k, v, dtype, 0.1, True, splits=2)
+    o, l = run(attn, q, k, v, dtype, S01, True, splits=2)
     gu.assert_close(o, ro, gu.TOL_H16, "decode Nq > Nk")
     gu.assert_lse(l, rl, gu.TOL_LSE_H16, "decode Nq > Nk")
     assert np.all(o[:, :, :8] == 0) and np.all(np.isneginf(l[:, :, :8]))
@@ -97,10 +102,10 @@ def test_decode_scattered_padding_unaligned_rows(attn, d, causal):
     mask = (rng.random((B, Nk)) < 0.01).astype(np.uint8)
     mask[1, :] = 1
     mask[2, :600] = 1
-    ro, rl = oracle.attn_kv(q64, k64, v64, 0.1, causal, mask)
+    ro, rl = oracle.attn_kv(q64, k64, v64, S01, causal, mask)
     for splits in (0, 3):
         say("decode scattered padding", d, causal, splits)
-        o, l = run(attn, q, k, v, "bf16", 0.1, causal, mask, splits)
+        o, l = run(attn, q, k, v, "bf16", S01, causal, mask, splits)
         gu.assert_close(o, ro, gu.TOL_H16, f"decode scattered padding d{d} causal={causal} splits {splits}")
         gu.assert_lse(l, rl, gu.TOL_LSE_H16, "decode scattered padding")
         assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))

@@ -55,8 +55,6 @@ def test_forward_and_cache_path_allocate_nothing(attn):
         run()
     after = free_bytes()
     assert after == before, f"free device memory changed by {before - after} bytes"
-    # the score matrix this shape would need in bf16 (4 GiB) was never held
-    assert N * N * H * 2 == 4 << 30
 
 
 def test_backward_allocates_nothing_beyond_its_outputs(attn):

@@ -54,10 +54,10 @@ def test_long_causal_forward_bf16(attn, N, d, H):
     p = synth.make_qkv(1, H, N, d, "bf16", 70)
     q, k, v = gu.upload(p)
     say("long forward", N, d, H)
-    o, l = attn.fwd(q, k, v, scale=d ** -0.5, causal=True, out_fp32=True)
+    o, l = attn.fwd(q, k, v, scale=float(np.float32(d ** -0.5)), causal=True, out_fp32=True)
     torch.cuda.synchronize()
     rows = synth.sample_rows(1, H, N, 12, 1)
-    check_rows(gu.host(o), gu.host(l), p, rows, d ** -0.5, True, gu.TOL_H16, gu.TOL_LSE_H16, f"long N{N} d{d}")
+    check_rows(gu.host(o), gu.host(l), p, rows, float(np.float32(d ** -0.5)), True, gu.TOL_H16, gu.TOL_LSE_H16, f"long N{N} d{d}")
 
 
 def test_long_forward_fp32(attn):
@@ -105,9 +105,9 @@ def test_long_key_value_cache(attn):
     k = synth.to_torch(kv.k, "bf16")
     v = synth.to_torch(kv.v, "bf16")
     say("long decode", Nk)
-    o, l = attn.decode_fwd(q, k, v, scale=d ** -0.5, causal=True, out_fp32=True)
+    o, l = attn.decode_fwd(q, k, v, scale=float(np.float32(d ** -0.5)), causal=True, out_fp32=True)
     torch.cuda.synchronize()
-    ro, rl = oracle.attn_kv(qp.q64, kv.k64, kv.v64, d ** -0.5, True)
+    ro, rl = oracle.attn_kv(qp.q64, kv.k64, kv.v64, float(np.float32(d ** -0.5)), True)
     gu.assert_close(gu.host(o), ro, gu.TOL_H16, "long decode")
     gu.assert_lse(gu.host(l), rl, gu.TOL_LSE_H16, "long decode")
 
@@ -138,11 +138,11 @@ def test_forward_beyond_2_31_elements(attn):
     assert H * N * d > 2 ** 31 and (H - 1) * N * d * 2 >= 2 ** 32
     say("forward beyond 2^31 elements", H, N, d)
     q, k, v, heads = _big_head_problem(H, N, d, 72)
-    o, l = attn.fwd(q, k, v, scale=d ** -0.5, causal=True, out_fp32=True)
+    o, l = attn.fwd(q, k, v, scale=float(np.float32(d ** -0.5)), causal=True, out_fp32=True)
     torch.cuda.synchronize()
     rows = synth.sample_rows(1, 1, N, 10, 2)
     for h, p in heads.items():
-        check_rows(gu.host(o[0, h][None, None]), gu.host(l[0, h][None, None]), p, rows, d ** -0.5, True,
+        check_rows(gu.host(o[0, h][None, None]), gu.host(l[0, h][None, None]), p, rows, float(np.float32(d ** -0.5)), True,
                    gu.TOL_H16, gu.TOL_LSE_H16, f"big head {h}")
     # a head in between holds zeros: every score is 0, so o = mean of zero rows = 0
     mid = gu.host(o[0, H // 2, ::4096])
@@ -160,10 +160,10 @@ def test_decode_beyond_2_31_elements(attn):
     _, k, v, heads = _big_head_problem(H, Nk, d, 73)
     qp = synth.make_qkv(1, H, 1, d, "bf16", 73, 2)
     q = gu.upload(qp)[0]
-    o, l = attn.decode_fwd(q, k, v, scale=d ** -0.5, out_fp32=True)
+    o, l = attn.decode_fwd(q, k, v, scale=float(np.float32(d ** -0.5)), out_fp32=True)
     torch.cuda.synchronize()
     for h, p in heads.items():
-        ro, rl = oracle.attn_kv(qp.q64[:, h:h + 1], p.k64, p.v64, d ** -0.5)
+        ro, rl = oracle.attn_kv(qp.q64[:, h:h + 1], p.k64, p.v64, float(np.float32(d ** -0.5)))
         gu.assert_close(gu.host(o[0, h]), ro[0, 0], gu.TOL_H16, f"decode big head {h}")
         gu.assert_lse(gu.host(l[0, h]), rl[0, 0], gu.TOL_LSE_H16, f"decode big head {h}")
     del q, k, v, o, l

@@ -384,3 +384,28 @@ def test_c4_sequence_sweep(attn, dtype):
             check_full(attn, p, 0.125, what=f"C4 {dtype} N{N}")
         else:
             sampled_check(attn, 1, 8, N, 64, dtype, False, 4, per_head=6)
+
+
+def test_c3_tile_and_order_sweep_at_its_shape(attn):
+    """The C3 sweep itself: B2 H16 N4096 d128 bf16, Q and K scaled by 4 (peaked
+    rows), non-causal, every Br x Bc in {16, 32, 64, 128}^2 in both fold orders
+    (32 runs), sampled rows of each run against the fp64 oracle at the 16-bit
+    gate on the fp32-output flavour."""
+    import torch
+    B, H, N, d = 2, 16, 4096, 128
+    p = synth.make_qkv(B, H, N, d, "bf16", 3, qk_factor=4.0)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    rows = gu.sample_rows(B, H, N, 8)
+    ro, rl = oracle.attn_rows(p.q64, p.k64, p.v64, scale, rows, False)
+    q, k, v = gu.upload(p)
+    worst = 0.0
+    for br, bc in TILES:
+        for order in (0, 1):
+            say("C3 sweep", br, bc, "order", order)
+            o, l = attn.fwd(q, k, v, scale=scale, out_fp32=True, br=br, bc=bc, kv_order=order)
+            torch.cuda.synchronize()
+            oh = gu.host(o).reshape(-1, d)[rows]
+            lh = gu.host(l).reshape(-1)[rows]
+            worst = max(worst, gu.assert_close(oh, ro, gu.TOL_H16, f"C3 {br}x{bc} order {order}"))
+            gu.assert_lse(lh, rl, gu.TOL_LSE_H16, f"C3 {br}x{bc} order {order}")
+    say(f"C3 sweep: worst max|d| {worst:.3e}")
