@@ -209,6 +209,16 @@ int attn_decode_fwd(const void* q, const void* k, const void* v, void* o, float*
                     const uint8_t* key_padding_mask, int dtype, void* stream,
                     void* workspace, size_t workspace_bytes, int num_splits);
 
+/* Measurement helper, not part of any computation: launches `reps` rounds of
+ * independent bf16 32x32x16 matrix-core products on every compute unit (eight
+ * four-wave workgroups per unit, accumulators in AGPRs, pseudo-random finite
+ * operands) and writes the launch's floating-point operation count to *flops.
+ * Timing it on `stream` gives the matrix-core rate the part sustains at its
+ * current clock: the ceiling the forward's rate is compared with, next to the
+ * published peak.  Returns ATTN_ERR_SHAPE for reps <= 0 or flops NULL and
+ * ATTN_ERR_HIP on a launch failure. */
+int attn_probe_mfma(int reps, void* stream, double* flops);
+
 /* Workspace bytes attn_decode_fwd needs for these sizes and num_splits
  * (0 for invalid sizes). */
 size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);

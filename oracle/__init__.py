@@ -38,6 +38,8 @@ def _load():
         lib.oracle_attn_bwd_f64.argtypes = [_D, _D, _D, _D, _D, _D, _D, L, L, L, L, D, I, _U8]
         lib.oracle_attn_blockmask_f64.argtypes = [_D, _D, _D, _D, _D, L, L, L, L, D, I, _U8, _U8, L]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_threads.argtypes = [I]
+        lib.oracle_set_threads.restype = None
         for f in (lib.oracle_attn_f64, lib.oracle_attn_rows_f64, lib.oracle_attn_blocked_f64,
                   lib.oracle_attn_blocked_kvouter_f64, lib.oracle_row_softmax_f64,
                   lib.oracle_row_blocked_f64, lib.oracle_num_threads, lib.oracle_attn_kv_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_blockmask_f64):
@@ -203,3 +205,8 @@ def attn_blockmask(q, k, v, scale, block_mask, block=64, causal=False, mask=None
 def num_threads():
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n):
+    """Threads of the oracle's parallel loops from now on (timing only)."""
+    _load().oracle_set_threads(int(n))

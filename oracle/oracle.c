@@ -540,3 +540,14 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* Threads of the parallel loops that follow (only for timing the oracle on
+ * one thread; the arithmetic of every routine is the same for any count). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

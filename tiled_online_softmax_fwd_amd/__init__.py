@@ -18,7 +18,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_HE
           8: "ATTN_ERR_ALIAS", 9: "ATTN_ERR_HIP", 10: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_sparse", "attn_check_args", "attn_default_tiles", "attn_naive_fwd",
            "attn_naive_workspace_bytes", "attn_decode_fwd", "attn_decode_workspace_bytes", "attn_decode_fwd_noalloc",
-           "attn_bwd", "attn_bwd_workspace_bytes",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_probe_mfma",
            "attn_status_string", "attn_last_error", "attn_version")
 
 
@@ -61,6 +61,8 @@ def lib():
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp, vp, ctypes.c_size_t]
         L.attn_bwd_workspace_bytes.argtypes = [i, i, i]
         L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_probe_mfma.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double)]
+        L.attn_probe_mfma.restype = ctypes.c_int
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         L.attn_last_error.argtypes = []
@@ -303,6 +305,16 @@ def check_args(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, scale, causal, m
     c = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib().attn_check_args(c(q_ptr), c(k_ptr), c(v_ptr), c(o_ptr), c(lse_ptr), B, H, N, d,
                                  float(scale), int(causal), c(mask_ptr), int(dtype), ctypes.byref(opts))
+
+
+def probe_mfma(reps, stream=None):
+    """Launch the matrix-core ceiling probe on the current stream; returns its
+    floating-point operation count (time it with events on the same stream)."""
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+    fl = ctypes.c_double()
+    _raise(lib().attn_probe_mfma(int(reps), ctypes.c_void_p(s), ctypes.byref(fl)))
+    return fl.value
 
 
 def version():

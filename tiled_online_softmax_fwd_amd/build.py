@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["attn_api.cpp", "naive.hip", "decode.hip", "bwd.hip", "fwd_inst_bf16.hip", "fwd_inst_f16.hip", "fwd_inst_f32.hip", "fwd_inst_sparse.hip"]
+SOURCES = ["attn_api.cpp", "naive.hip", "decode.hip", "bwd.hip", "fwd_inst_bf16.hip", "fwd_inst_f16.hip", "fwd_inst_f32.hip", "fwd_inst_sparse.hip", "probe.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:
