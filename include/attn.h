@@ -43,12 +43,20 @@
  *     softmax over the visible keys, both exact).
  *   - stream: a hipStream_t passed as void*; NULL is the null stream.  Every
  *     call is asynchronous on that stream; outputs are valid once the caller
- *     has synchronised it.  No entry point synchronises, allocates device
- *     memory, or keeps state beyond a thread-local error string.
+ *     has synchronised it.  No entry point synchronises or allocates device
+ *     memory.  State kept between calls: a thread-local error string, the
+ *     compute-unit count of each device (queried once, for the grid), the
+ *     ATTN_TRACE setting, and the device scratch of attn_decode_fwd_noalloc.
  *   - Errors: arguments are checked on the host before anything is launched; a
  *     failed check returns its status and writes nothing.  A launch failure
  *     returns ATTN_ERR_HIP.  attn_last_error() then holds a message.  No
  *     exception and no abort crosses this interface.
+ *   - Dispatch log: with the environment variable ATTN_TRACE set to anything
+ *     but "" or "0" when the library first reads it, every entry point except
+ *     attn_check_args writes one line starting "attn: " to stderr: the
+ *     kernel instance it launched (type, head size, tiles), the shape, the
+ *     loop form, the grid and block, or the status it returned without a
+ *     launch.
  *   - Determinism: identical inputs and options give bitwise-identical o and
  *     lse (no atomics, fixed reduction order).
  */
@@ -81,10 +89,10 @@ enum attn_status {
     ATTN_ERR_DTYPE = 4,     /* unknown dtype                                            */
     ATTN_ERR_ALIGN = 5,     /* q/k/v/o not 16-byte aligned, or lse not 4-byte aligned   */
     ATTN_ERR_TILE = 6,      /* tile shape, kv_order or ref_slack not supported          */
-    ATTN_ERR_SCALE = 7,     /* scale not finite or not > 0                              */
+    ATTN_ERR_SCALE = 7,     /* scale not finite                                         */
     ATTN_ERR_ALIAS = 8,     /* o overlaps an input or lse                               */
     ATTN_ERR_HIP = 9,       /* the HIP runtime reported an error                        */
-    ATTN_ERR_WORKSPACE = 10 /* naive baseline: workspace NULL or too small              */
+    ATTN_ERR_WORKSPACE = 10 /* workspace NULL, misaligned or too small                   */
 };
 
 /* Tile and fold-order options (attn_fwd_ex).
