@@ -259,6 +259,30 @@ def test_scattered_padding_with_unaligned_mask_rows(attn, dtype, d, causal):
         assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
 
 
+@pytest.mark.parametrize("dtype,d,br,bc", [("f32", 128, 128, 128), ("f32", 64, 32, 128), ("f32", 128, 16, 64),
+                                            ("f32", 64, 64, 16), ("bf16", 128, 16, 32), ("f16", 64, 128, 16)])
+def test_scattered_padding_fp32_and_16_row_tiles(attn, dtype, d, br, bc):
+    """The padding cases above through the fp32 single-buffer kernel (128-key
+    tiles at d = 128), the fp32 double-buffered kernel at 128-key tiles and the
+    16-row/16-key kernel: tiles without a padded key take the unmasked path,
+    wholly padded tiles are skipped, the rest read the flags as words (or
+    bytes, where the mask row is not 4-byte aligned)."""
+    N = 301
+    p = synth.make_qkv(4, 2, N, d, dtype, 8)
+    rng = np.random.default_rng([8, N, 99])
+    mask = (rng.random((4, N)) < 0.01).astype(np.uint8)
+    mask[1, :] = 1
+    mask[2, :200] = 1
+    scale = float(np.float32(1 / math.sqrt(d)))
+    for causal in (False, True):
+        for order in (0, 1):
+            say("scattered padding tiles", dtype, d, br, bc, "causal", causal, "order", order)
+            e, o, l, ro, rl = check_full(attn, p, scale, causal, mask,
+                                         f"{dtype} d{d} {br}x{bc} causal={causal} o{order}",
+                                         br=br, bc=bc, kv_order=order)
+            assert np.all(o[1] == 0) and np.all(np.isneginf(l[1]))
+
+
 # ------------------------------------------------------------------ edges
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])

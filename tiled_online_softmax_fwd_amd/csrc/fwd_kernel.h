@@ -107,6 +107,40 @@ __device__ __forceinline__ u32x4 q_mode16(u32x4 w, int qmode)
 }
 __device__ __forceinline__ float q_mode32(float x, int qmode) { return qmode == 1 ? -x : (qmode == 2 ? 0.f : x); }
 
+// Key-padding flags of the four consecutive keys k..k+3 of one mask row, as
+// the bytes of one word: one 32-bit load when the row is 4-byte aligned and
+// the four keys lie inside it, else four byte loads at keys clamped to N - 1
+// (keys past N are never visible, and key N - 1 lies in the same tile).
+__device__ __forceinline__ uint32_t pad_word(const uint8_t* row, bool vec, int k, int N)
+{
+    if (vec && k + 3 < N) return *(const uint32_t*)(row + k);
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w |= (uint32_t)row[min(k + r, N - 1)] << (8 * r);
+    return w;
+}
+// Non-zero when some byte of w is zero (some of the four keys is not padded).
+__device__ __forceinline__ uint32_t has_zero_byte(uint32_t w) { return (w - 0x01010101u) & ~w & 0x80808080u; }
+// Byte j of w is zero: key j of the word is not padded.
+__device__ __forceinline__ bool unpadded(uint32_t w, int j) { return ((w >> (8 * j)) & 0xffu) == 0; }
+
+// Tile-level padding decision of one wave over the flag words of the keys its
+// lanes hold (together every key of the tile): `any` when some key is padded
+// (the tile takes the masked path), `none_visible` when every key is (the
+// tile adds nothing: its maximum is -inf and every P is 0).
+template <int NWORDS>
+__device__ __forceinline__ void pad_tile(const uint32_t (&w)[NWORDS], bool& any, bool& none_visible)
+{
+    uint32_t a = 0, z = 0;
+#pragma unroll
+    for (int i = 0; i < NWORDS; ++i) {
+        a |= w[i];
+        z |= has_zero_byte(w[i]);
+    }
+    any = __builtin_amdgcn_ballot_w64(a != 0) != 0;
+    none_visible = __builtin_amdgcn_ballot_w64(z != 0) == 0;
+}
+
 // Reference of the online merge.  The merge multiplies l and acc by
 // exp(m_old - m_new) when the reference moves from m_old to m_new, and the
 // result acc / l (and lse = m + ln l) is the same for any reference as long as
@@ -941,11 +975,20 @@ fwd_m32_f32(FwdParams p)
     const int wave_q0 = q0 + wave * 32;
     const float c = p.c;
     const float* svf = (const float*)sv;
+    // key-padding flags: word (kb, g4) holds keys k0 + 32 kb + 8 g4 + 4 hh + 0..3
+    const uint8_t* const prow = p.mask ? p.mask + (size_t)b * N : nullptr;
+    const bool pvec = prow && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[NKB * 4];
 
     for (int it = 0; it < kt_end; ++it) {
         const int kt = p.kv_order ? (kt_end - 1 - it) : it;
         const int k0 = kt * BC;
         const int rows_valid = min(BC, N - k0);
+        // the flags load while the tile is staged
+        if (prow) {
+#pragma unroll
+            for (int w = 0; w < NKB * 4; ++w) padw[w] = pad_word(prow, pvec, k0 + (w >> 2) * 32 + 8 * (w & 3) + 4 * hh, N);
+        }
         __syncthreads();
         stage_tile<BC, CPR, NT, 0>(sk, (const u32x4*)(K + (size_t)k0 * D), rows_valid, tid);
         stage_tile<BC, CPR, NT, 2>(sv, (const u32x4*)(V + (size_t)k0 * D), rows_valid, tid);
@@ -953,6 +996,13 @@ fwd_m32_f32(FwdParams p)
         // causal: every key of the tile comes after every row of the wave
         // (the wave took part in the staging and both barriers)
         if (p.causal && k0 > wave_q0 + 31) continue;
+        // padding: only tiles with a padded key take the masked path, and a
+        // tile whose keys are all padded adds nothing
+        bool pad_any = false, pad_all = false;
+        if (prow) {
+            pad_tile(padw, pad_any, pad_all);
+            if (pad_all) continue;
+        }
 
         f32x16 s[NKB];
 #pragma unroll
@@ -968,7 +1018,7 @@ fwd_m32_f32(FwdParams p)
             }
         }
 
-        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
+        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || pad_any;
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -977,7 +1027,7 @@ fwd_m32_f32(FwdParams p)
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
                     bool vis = key < N;
                     if (p.causal) vis = vis && key <= qi;
-                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    if (pad_any) vis = vis && unpadded(padw[kb * 4 + (j >> 2)], j & 3);
                     if (!vis) s[kb][j] = -INFINITY;
                 }
             }
@@ -1106,6 +1156,17 @@ fwd_m32_f32_db(FwdParams p)
     for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
     const float c = p.c;
 
+    // key-padding flags: word (kb, g4) holds keys k0 + 32 kb + 8 g4 + 4 hh +
+    // 0..3; padw for the current tile, padn for the next one
+    const uint8_t* const prow = p.mask ? p.mask + (size_t)b * N : nullptr;
+    const bool pvec = prow && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[NKB * 4], padn[NKB * 4];
+    auto load_pad = [&](int k1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int w = 0; w < NKB * 4; ++w) padn[w] = pad_word(prow, pvec, k1 + (w >> 2) * 32 + 8 * (w & 3) + 4 * hh, N);
+    };
+    if (prow) load_pad(tile_at(0) * BC);
+
     auto body = [&](auto BUF, int it) __attribute__((always_inline)) {
         constexpr int buf = decltype(BUF)::value;
         const int k0 = tile_at(it) * BC;
@@ -1117,8 +1178,17 @@ fwd_m32_f32_db(FwdParams p)
             kplan.issue(sk[buf ^ 1], K, tile_at(it + 1) * BC, N, wave);
             vplan.issue(sv[buf ^ 1], V, tile_at(it + 1) * BC, N, wave);
         }
-        // causal: every key of the tile comes after every row of the wave
-        if (p.causal && k0 > wave_q0 + 31) return;
+        // this tile's flags arrived with the wait above; fetch the next tile's
+        bool pad_any = false, pad_all = false;
+        if (prow) {
+#pragma unroll
+            for (int w = 0; w < NKB * 4; ++w) padw[w] = padn[w];
+            if (it + 1 < kt_end) load_pad(tile_at(it + 1) * BC);
+            pad_tile(padw, pad_any, pad_all);
+        }
+        // causal: every key of the tile comes after every row of the wave;
+        // padding: every key of the tile padded
+        if ((p.causal && k0 > wave_q0 + 31) || pad_all) return;
 
         f32x16 s[NKB];
 #pragma unroll
@@ -1136,7 +1206,7 @@ fwd_m32_f32_db(FwdParams p)
 
         // invisible scores -> -inf; element (kb, j) is key k0 + 32*kb + 8*(j/4) + 4*hh + j%4.
         // Rows of the ragged last tile past N hold row N-1's data (finite).
-        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || (p.mask != nullptr);
+        const bool need_mask = (p.causal && k0 + BC - 1 > wave_q0) || (k0 + BC > N) || pad_any;
         if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -1145,7 +1215,7 @@ fwd_m32_f32_db(FwdParams p)
                     const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
                     bool vis = key < N;
                     if (p.causal) vis = vis && key <= qi;
-                    if (vis && p.mask) vis = p.mask[(size_t)b * N + key] == 0;
+                    if (pad_any) vis = vis && unpadded(padw[kb * 4 + (j >> 2)], j & 3);
                     if (!vis) s[kb][j] = -INFINITY;
                 }
             }

@@ -120,11 +120,19 @@ fwd_m16(FwdParams p)
     int kt_end = nkt;
     if (p.causal) kt_end = min(nkt, (min(q0 + BR, N) - 1) / BC + 1);
     const float c = p.c;
-    const uint8_t* mrow = p.mask ? p.mask + (size_t)b * N : nullptr;
+    // key-padding flags: word kb holds keys k0 + 16 kb + 4 g + 0..3
+    const uint8_t* const prow = p.mask ? p.mask + (size_t)b * N : nullptr;
+    const bool pvec = prow && ((uintptr_t)prow & 3u) == 0;
+    uint32_t padw[NKB];
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
     for (int it = 0; it < kt_end; ++it) {
         const int k0 = (p.kv_order ? (kt_end - 1 - it) : it) * BC;
+        // the flags load while the tile is staged
+        if (prow) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) padw[kb] = pad_word(prow, pvec, k0 + kb * 16 + 4 * g, N);
+        }
 
         // stage K and V rows k0..k0+BC-1 (rows past N-1 repeat row N-1; their
         // scores are masked below)
@@ -143,6 +151,16 @@ fwd_m16(FwdParams p)
             }
         }
         __syncthreads();
+        // causal: every key of the tile comes after every row of the wave;
+        // padding: only tiles with a padded key take the masked path, and a
+        // tile whose keys are all padded adds nothing (the wave took part in
+        // the staging and both barriers)
+        if (p.causal && k0 > q0 + wave * 16 + 15) continue;
+        bool pad_any = false, pad_all = false;
+        if (prow) {
+            pad_tile(padw, pad_any, pad_all);
+            if (pad_all) continue;
+        }
 
         // S^T = K Q^T, 16 keys x 16 queries per block
         f32x4 s[NKB];
@@ -168,14 +186,14 @@ fwd_m16(FwdParams p)
         }
 
         // visibility: accumulator element (kb, i) of this lane is key k0 + 16*kb + 4*g + i
-        if (p.causal || p.mask || k0 + BC > N) {
+        if (p.causal || pad_any || k0 + BC > N) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = k0 + kb * 16 + 4 * g + i;
                     bool vis = key < N && (!p.causal || key <= qi);
-                    if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
+                    if (pad_any) vis = vis && unpadded(padw[kb], i);
                     if (!vis) s[kb][i] = -INFINITY;
                 }
             }
