@@ -22,9 +22,12 @@
 //             layout of dQ^T += K^T dS^T (K^T read transposed from LDS).
 // Products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation; P and
 // dS are rounded to the input type for the MFMA, as P is in the forward.
+// Tiles read both row-wise and transposed (Q and dO here, K in bwd_dq) are
+// stored with swz_kt, under which neither read has LDS bank conflicts.
 #include <hip/hip_runtime.h>
 #include "bwd.h"
 #include "fwd_kernel.h"
+
 
 namespace attnk {
 
@@ -54,23 +57,40 @@ __global__ void __launch_bounds__(256) bwd_pre(BwdParams p)
     }
 }
 
-// Transposing LDS read of the 32x32x16 operand that holds, for lane
+// Transposing LDS reads of the 32x32x16 operand that holds, for lane
 // (column c = lane % 32 of the 32-column block db, half hh = lane / 32),
 // tile[rows 16*ks2 + 4*hh + 0..3 and + 8 .. + 11][32*db + c] of a row-major
-// tile stored with the swz_k chunk swizzle.
-template <int CPR>
-__device__ __forceinline__ u32x4 tr_operand(const void* tile, int ks2, int db, int lane)
+// tile stored with the swz_kt chunk swizzle (every tile the backward reads
+// transposed is also read row-wise; swz_kt serves both without conflicts).
+// The swizzle's row term depends on the row within its 16-row group only, so
+// the per-lane byte offsets of the two 8-byte reads are fixed for each db
+// (TrOffsets, computed once) and 16*ks2 rows add an immediate.
+template <int CPR, int DB>
+struct TrOffsets {
+    uint32_t off[2][DB];
+    __device__ __forceinline__ void init(int lane)
+    {
+        const int hh = lane >> 5, g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = 4 * hh + rsrc + 8 * t;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int chunk = db * 4 + 2 * g + (qsrc >> 1);
+                off[t][db] = (uint32_t)((row * CPR + swz_kt<CPR>(row, chunk)) * 16 + (qsrc & 1) * 8);
+            }
+        }
+    }
+};
+
+template <int CPR, int DB>
+__device__ __forceinline__ u32x4 tr_operand(const void* tile, const TrOffsets<CPR, DB>& to, int ks2, int db)
 {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    typedef __attribute__((address_space(3))) char lds_char;
-    const int hh = lane >> 5, g = (lane >> 4) & 1, rsrc = (lane & 15) >> 2, qsrc = lane & 3;
-    const int chunk = db * 4 + 2 * g + (qsrc >> 1);
-    const int row1 = ks2 * 16 + 4 * hh + rsrc, row2 = row1 + 8;
-    lds_char* base = (lds_char*)tile;
-    const int off1 = (row1 * CPR + swz_k<CPR>(row1, chunk)) * 16 + (qsrc & 1) * 8;
-    const int off2 = (row2 * CPR + swz_k<CPR>(row2, chunk)) * 16 + (qsrc & 1) * 8;
-    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off1));
-    const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off2));
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)tile +
+                          (uint32_t)(ks2 * 16 * CPR * 16);
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[0][db]));
+    const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[1][db]));
     const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
     return (u32x4){w1[0], w1[1], w2[0], w2[1]};
 }
@@ -85,19 +105,23 @@ __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
     return r;
 }
 
-// MASKED (calls with a key-padding mask): a wave whose 32 keys are all padded
+// KB key blocks of 32 per wave (KW = 32*KB keys): the Q and dO operands a
+// wave reads from LDS (row-major for S and dP, transposed for dK and dV) serve
+// all KB blocks, so LDS bytes per matrix product fall as KB grows (at d = 128,
+// KB = 2 needs four waves, one per SIMD, with 256 accumulator registers).
+// MASKED (calls with a key-padding mask): a wave whose keys are all padded
 // takes part in the copies and barriers only (its dK and dV stay zero).
-template <typename T, int D, int NW, bool MASKED = false>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+template <typename T, int D, int NW, int KB, bool MASKED = false>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KB == 1 ? NW / 4 : 1, KB == 1 ? NW / 4 : 1)))
 bwd_dkdv(BwdParams p)
 {
     using TR = H16<T>;
     using v8 = typename TR::v8;
-    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 64, NH = BQ / 32;
-    using Plan = TilePlan<BQ, CPR, NW, 0>;
+    constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 64, NH = BQ / 32, KW = 32 * KB;
+    using Plan = TilePlan<BQ, CPR, NW, 3>;
     __shared__ u32x4 sq[2][BQ * CPR];
     __shared__ u32x4 sg[2][BQ * CPR];
-    __shared__ u32x4 s_vw[NW][DK][64];   // each wave's V^T operands (registers are short)
+    __shared__ u32x4 s_vw[NW][KB][DK][64];   // each wave's V^T operands (registers are short)
     __shared__ __attribute__((aligned(16))) float s_l2[2][BQ];
     __shared__ __attribute__((aligned(16))) float s_d[2][BQ];
 
@@ -115,35 +139,53 @@ bwd_dkdv(BwdParams p)
     const T* __restrict__ G = (const T*)p.dout + head;
     const float* __restrict__ L2 = p.lse2 + (size_t)bh * N;
     const float* __restrict__ DS = p.dsum + (size_t)bh * N;
-    const int k_wave = kt * 32 * NW + wave * 32;      // first key of this wave
-    const int key = k_wave + col;                     // this lane's key
-    const int krow = min(key, N - 1);
-    const bool key_on = key < N && !(p.mask && p.mask[(size_t)b * N + krow]);
-    const bool keys_all_on = __builtin_amdgcn_ballot_w64(key_on) == ~0ull;   // wave-uniform
-    const bool keys_all_off = MASKED && __builtin_amdgcn_ballot_w64(key_on) == 0;
+    const int k_wave = kt * KW * NW + wave * KW;      // first key of this wave
+    // this lane's key in block kb: k_wave + 32 kb + col
+    bool key_on[KB];
+    bool any_on = false, all_on = true;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int key = k_wave + 32 * kb + col;
+        const int krow = min(key, N - 1);
+        key_on[kb] = key < N && !(p.mask && p.mask[(size_t)b * N + krow]);
+        any_on = any_on || key_on[kb];
+        all_on = all_on && key_on[kb];
+    }
+    const bool keys_all_on = __builtin_amdgcn_ballot_w64(all_on) == ~0ull;   // wave-uniform
+    const bool keys_all_off = MASKED && __builtin_amdgcn_ballot_w64(any_on) == 0;
 
-    // K^T and V^T operands of this lane's key: head columns 16*ks + 8*hh + 0..7.
+    // K^T and V^T operands of the lane's keys: head columns 16*ks + 8*hh + 0..7.
     // K^T stays in registers; V^T goes to the wave's own LDS slots (each lane
     // reads back only what it wrote), which keeps the loop free of spills.
-    u32x4 kw[DK];
+    u32x4 kw[KB][DK];
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-        kw[ks] = *(const u32x4*)(K + (size_t)krow * D + ks * 16 + hh * 8);
-        s_vw[wave][ks][lane] = *(const u32x4*)(V + (size_t)krow * D + ks * 16 + hh * 8);
+    for (int kb = 0; kb < KB; ++kb) {
+        const int krow = min(k_wave + 32 * kb + col, N - 1);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            kw[kb][ks] = *(const u32x4*)(K + (size_t)krow * D + ks * 16 + hh * 8);
+            s_vw[wave][kb][ks][lane] = *(const u32x4*)(V + (size_t)krow * D + ks * 16 + hh * 8);
+        }
     }
 #pragma unroll
-    for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(kw[ks]));
-
-    f32x16 dk[DB], dv[DB];
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dk[db] = (f32x16){}; dv[db] = (f32x16){}; }
+        for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(kw[kb][ks]));
+
+    f32x16 dk[KB][DB], dv[KB][DB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) { dk[kb][db] = (f32x16){}; dv[kb][db] = (f32x16){}; }
 
     // query tiles that can see any key of the workgroup
-    const int k_wg = kt * 32 * NW;
+    const int k_wg = kt * KW * NW;
     const int qt0 = p.causal ? k_wg / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
     Plan plan;
     plan.init(wave, lane);
+    TrOffsets<CPR, DB> tro;
+    tro.init(lane);
     const float c = p.c;
 
     auto stage = [&](int buf, int qt) __attribute__((always_inline)) {
@@ -188,12 +230,17 @@ bwd_dkdv(BwdParams p)
             // the wave has nothing to add (it still took part in the copy above)
             if (p.causal && qh + 31 < k_wave) continue;
 
-            // S = Q K^T: lane holds key column `col`, query rows 8*(j/4) + 4*hh + j%4
-            f32x16 s = (f32x16){};
+            // S = Q K^T: lane holds key column `col` of block kb, query rows
+            // 8*(j/4) + 4*hh + j%4; each Q operand serves every key block
+            f32x16 s[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
-                const u32x4 qa = sq[buf][(32 * h + col) * CPR + swz_k<CPR>(32 * h + col, ks * 2 + hh)];
-                s = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[ks]), s);
+                const u32x4 qa = sq[buf][(32 * h + col) * CPR + swz_kt<CPR>(32 * h + col, ks * 2 + hh)];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    s[kb] = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[kb][ks]), s[kb]);
             }
             // lse2 of the lane's 16 query rows: four 16-byte LDS reads
             f32x4 l2v[4];
@@ -204,65 +251,88 @@ bwd_dkdv(BwdParams p)
             // per-element branch.  Pairs that are not visible are then set to 0,
             // on tiles that are not wholly visible only.
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                s[j] = fast_exp2(fmaf(s[j], c, -l2v[j >> 2][j & 3]));
-                asm volatile("" : "+v"(s[j]));
-            }
-            const bool all = keys_all_on && qh + 32 <= N && (!p.causal || qh >= k_wave + 31);
-            if (!all) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int qi = qh + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    bool vis = key_on && qi < N;
-                    if (p.causal) vis = vis && key <= qi;
-                    s[j] = vis ? s[j] : 0.f;
+                    s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2v[j >> 2][j & 3]));
+                    asm volatile("" : "+v"(s[kb][j]));
                 }
+            const bool all = keys_all_on && qh + 32 <= N && (!p.causal || qh >= k_wave + KW - 1);
+            if (!all) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int qi = qh + 8 * (j >> 2) + 4 * hh + (j & 3);
+                        bool vis = key_on[kb] && qi < N;
+                        if (p.causal) vis = vis && k_wave + 32 * kb + col <= qi;
+                        s[kb][j] = vis ? s[kb][j] : 0.f;
+                    }
             }
-            const v8 pa0 = pack8<T>(s, 0), pa1 = pack8<T>(s, 1);
+            v8 pa[KB][2];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) { pa[kb][0] = pack8<T>(s[kb], 0); pa[kb][1] = pack8<T>(s[kb], 1); }
             // dV += P^T dO (contraction over the half's 32 queries)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dv[db] = TR::mma32(pa0, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 2 * h, db, lane)), dv[db]);
-                dv[db] = TR::mma32(pa1, __builtin_bit_cast(v8, tr_operand<CPR>(sg[buf], 2 * h + 1, db, lane)), dv[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const v8 gt = __builtin_bit_cast(v8, tr_operand(sg[buf], tro, 2 * h + t, db));
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) dv[kb][db] = TR::mma32(pa[kb][t], gt, dv[kb][db]);
+                }
             // dP = dO V^T, then dS = P (dP - D) in place
-            f32x16 dp = (f32x16){};
+            f32x16 dp[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) dp[kb] = (f32x16){};
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
-                const u32x4 ga = sg[buf][(32 * h + col) * CPR + swz_k<CPR>(32 * h + col, ks * 2 + hh)];
-                dp = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][ks][lane]), dp);
+                const u32x4 ga = sg[buf][(32 * h + col) * CPR + swz_kt<CPR>(32 * h + col, ks * 2 + hh)];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    dp[kb] = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][kb][ks][lane]), dp[kb]);
             }
             // D of the same rows, read where it is used
             f32x4 dsv[4];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) dsv[g4] = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
+            v8 da[KB][2];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) dp[j] = s[j] * (dp[j] - dsv[j >> 2][j & 3]);
-            const v8 da0 = pack8<T>(dp, 0), da1 = pack8<T>(dp, 1);
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) dp[kb][j] = s[kb][j] * (dp[kb][j] - dsv[j >> 2][j & 3]);
+                da[kb][0] = pack8<T>(dp[kb], 0);
+                da[kb][1] = pack8<T>(dp[kb], 1);
+            }
             // dK += dS^T Q
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dk[db] = TR::mma32(da0, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 2 * h, db, lane)), dk[db]);
-                dk[db] = TR::mma32(da1, __builtin_bit_cast(v8, tr_operand<CPR>(sq[buf], 2 * h + 1, db, lane)), dk[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const v8 qt_ = __builtin_bit_cast(v8, tr_operand(sq[buf], tro, 2 * h + t, db));
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) dk[kb][db] = TR::mma32(da[kb][t], qt_, dk[kb][db]);
+                }
         }
     }
 
-    // dV[key][d] and dK[key][d]: accumulator block db holds head column
-    // 32*db + col and keys 8*(j/4) + 4*hh + j%4 of the wave's 32 keys
+    // dV[key][d] and dK[key][d]: accumulator block (kb, db) holds head column
+    // 32*db + col and keys 32*kb + 8*(j/4) + 4*hh + j%4 of the wave's keys
     const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int kr = k_wave + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (kr < N) {
-                const size_t idx = head + (size_t)kr * D + 32 * db + col;
-                p.dv[idx] = dv[db][j];
-                p.dk[idx] = dk[db][j] * sc;
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int kr = k_wave + 32 * kb + 8 * (j >> 2) + 4 * hh + (j & 3);
+                if (kr < N) {
+                    const size_t idx = head + (size_t)kr * D + 32 * db + col;
+                    p.dv[idx] = dv[kb][db][j];
+                    p.dk[idx] = dk[kb][db][j] * sc;
+                }
             }
         }
-    }
 }
 
 // MASKED (calls with a key-padding mask): each lane's padding flags of the next
@@ -276,7 +346,9 @@ bwd_dq(BwdParams p)
     using TR = H16<T>;
     using v8 = typename TR::v8;
     constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BC = 64, NKB = BC / 32, KS = BC / 16;
-    using Plan = TilePlan<BC, CPR, NW, 0>;
+    // K tiles are read row-wise and transposed, V tiles row-wise: both use
+    // swz_kt, so one copy plan serves both
+    using Plan = TilePlan<BC, CPR, NW, 3>;
     __shared__ u32x4 sk[2][BC * CPR];
     __shared__ u32x4 sv[2][BC * CPR];
 
@@ -343,6 +415,8 @@ bwd_dq(BwdParams p)
     const int kt_end = p.causal ? min(nkt, (min(q0 + 32 * NW, N) - 1) / BC + 1) : nkt;
     Plan plan;
     plan.init(wave, lane);
+    TrOffsets<CPR, DB> tro;
+    tro.init(lane);
     const float c = p.c;
     if (kt_end > 0) {
         plan.issue(sk[0], K, 0, N, wave);
@@ -388,8 +462,8 @@ bwd_dq(BwdParams p)
             const int r = kb * 32 + col;
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
-                const u32x4 ka = sk[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
-                const u32x4 va = sv[buf][r * CPR + swz_k<CPR>(r, ks * 2 + hh)];
+                const u32x4 ka = sk[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
+                const u32x4 va = sv[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
                 s[kb] = TR::mma32(__builtin_bit_cast(v8, ka), __builtin_bit_cast(v8, qw[ks]), s[kb]);
                 dp[kb] = TR::mma32(__builtin_bit_cast(v8, va), __builtin_bit_cast(v8, gw[ks]), dp[kb]);
             }
@@ -430,7 +504,7 @@ bwd_dq(BwdParams p)
             const v8 da = pack8<T>(s[ks2 >> 1], ks2 & 1);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const u32x4 ka = tr_operand<CPR>(sk[buf], ks2, db, lane);
+                const u32x4 ka = tr_operand(sk[buf], tro, ks2, db);
                 dq[db] = TR::mma32(__builtin_bit_cast(v8, ka), da, dq[db]);
             }
         }
@@ -462,12 +536,19 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t st)
     hipLaunchKernelGGL((bwd_pre<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned tiles = (unsigned)((p.N + 32 * NW - 1) / (32 * NW));
-    const dim3 grid((unsigned)(p.B * p.H) * tiles), block(NW * 64);
-    if (p.mask) hipLaunchKernelGGL((bwd_dkdv<T, D, NW, true>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((bwd_dkdv<T, D, NW, false>), grid, block, 0, st, p);
+    // dK, dV: waves of 32 keys.  Waves of 64 keys (KB = 2, four per
+    // workgroup, one per SIMD) read 43% fewer LDS bytes but measured 8% slower
+    // at B1 H32 N8192 d128 causal on MI355X: one wave per SIMD leaves the LDS
+    // and exponential latencies of each 32-query step exposed.
+    constexpr int KB = 1, NWK = NW;
+    const unsigned ktiles = (unsigned)((p.N + 32 * KB * NWK - 1) / (32 * KB * NWK));
+    const dim3 kgrid((unsigned)(p.B * p.H) * ktiles), kblock(NWK * 64);
+    if (p.mask) hipLaunchKernelGGL((bwd_dkdv<T, D, NWK, KB, true>), kgrid, kblock, 0, st, p);
+    else hipLaunchKernelGGL((bwd_dkdv<T, D, NWK, KB, false>), kgrid, kblock, 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const unsigned tiles = (unsigned)((p.N + 32 * NW - 1) / (32 * NW));
+    const dim3 grid((unsigned)(p.B * p.H) * tiles), block(NW * 64);
     if (p.mask) hipLaunchKernelGGL((bwd_dq<T, D, NW, true>), grid, block, 0, st, p);
     else hipLaunchKernelGGL((bwd_dq<T, D, NW, false>), grid, block, 0, st, p);
     return hipGetLastError();

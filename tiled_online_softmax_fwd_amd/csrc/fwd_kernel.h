@@ -197,6 +197,18 @@ template <int CPR> __device__ __forceinline__ int swz_v16(int r, int c)
 }
 // fp32 V rows are read 4 bytes per lane, 32 lanes on one row and 32 on row+4.
 __device__ __forceinline__ int swz_v32(int r, int c) { return c ^ (((r >> 2) & 1) << 3); }
+// 16-bit rows read both ways (the backward's Q, dO and K tiles): 16 bytes per
+// lane down 16 consecutive rows, and transposed, a half wave over 4 rows x 64
+// bytes.  The row term is a bijection over each 16-row group (the row reads
+// hit distinct 16-byte groups) whose top two bits are r & 3 (the 4 rows of a
+// transposed read land in 4 distinct 64-byte groups).  At 8 chunks per row
+// (two rows per 256 bytes) the row term is a bijection of r >> 1 over rows of
+// one parity, whose top bit is (r >> 1) & 1.
+template <int CPR> __device__ __forceinline__ int swz_kt(int r, int c)
+{
+    if constexpr (CPR >= 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 // Cooperative copy of ROWS x CPR 16-byte chunks from global rows (row stride
 // CPR chunks) into LDS at chunk index r*CPR + SWZ(r, c).  Rows >= rows_valid are
@@ -226,6 +238,7 @@ __device__ __forceinline__ void stage_tile(u32x4* __restrict__ lds, const u32x4*
                 int sc;
                 if constexpr (KIND == 0) sc = swz_k<CPR>(r, c);
                 else if constexpr (KIND == 1) sc = swz_v16<CPR>(r, c);
+                else if constexpr (KIND == 3) sc = swz_kt<CPR>(r, c);
                 else sc = swz_v32(r, c);
                 lds[r * CPR + sc] = buf[u];
             }
@@ -379,7 +392,8 @@ struct TilePlan {
         for (int i = 0; i < NI; ++i) {
             const int p = (wave * NI + i) * 64 + lane;
             const int r = p / CPR, pc = p % CPR;
-            const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : (KIND == 1) ? swz_v16<CPR>(r, pc) : swz_v32(r, pc);
+            const int c = (KIND == 0) ? swz_k<CPR>(r, pc) : (KIND == 1) ? swz_v16<CPR>(r, pc)
+                        : (KIND == 3) ? swz_kt<CPR>(r, pc) : swz_v32(r, pc);
             row[i] = r;
             off[i] = (uint32_t)(r * CPR + c) * 16u;
         }
