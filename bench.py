@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (MI355X spec)
 METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak; max|Δ| vs FP64 oracle"
-KERNEL_SOURCES = ["fwd_kernel.h"]      # default sources of a traffic record (the forward kernels)
+# default sources of a traffic record: the forward kernels, the generated
+# pipeline and the host planner (which picks tiles and the persistent grid)
+KERNEL_SOURCES = ["fwd_kernel.h", "fwd_pipe_asm.h", "attn_host.h"]
 
 
 def kernel_hash(sources=None):

@@ -266,7 +266,10 @@ __device__ __forceinline__ void tile_of_block(const FwdParams& p, int& bh, int& 
 // equal work.  With xcd_affine, the items of head bh go to the workgroups of
 // XCD bh % 8 (workgroups are dealt to the 8 XCDs round-robin), so every head's
 // K and V are read through one XCD's L2, and the workgroups of a head sweep its
-// key tiles together (heaviest tile of each pair first).
+// key tiles together (heaviest tile of each pair first: its phase reads the
+// same key tile in every workgroup of the head at once; light tile first
+// staggers them, and 32 distinct tiles per step overflow the XCD's L2 -- 1.68x
+// the reads of heavy first at B1 H32 N8192 d128 causal on MI355X).
 struct UnitSched {
     int item, stride, n_items, iph, n_qt, causal, xcd, part;
 
