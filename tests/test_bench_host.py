@@ -55,7 +55,8 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
     csrc = tmp_path / "tiled_online_softmax_fwd_amd" / "csrc"
     csrc.mkdir(parents=True)
     (tmp_path / "profiles").mkdir()
-    (csrc / "fwd_kernel.h").write_text("forward v1")
+    for f in bench.KERNEL_SOURCES:
+        (csrc / f).write_text(f"{f} v1")
     (csrc / "decode.hip").write_text("decode v1")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     recs = {"fwd": {"kernel_hash": bench.kernel_hash(), "hbm_bytes_per_launch": 1.0},
@@ -65,6 +66,11 @@ def test_traffic_record_follows_its_sources(tmp_path, monkeypatch):
     assert bench.traffic_record("fwd")["hbm_bytes_per_launch"] == 1.0
     assert bench.traffic_record("dec")["hbm_bytes_per_launch"] == 2.0
     assert bench.traffic_record("missing") is None
+    for f in bench.KERNEL_SOURCES:     # a change to any default source drops the record
+        (csrc / f).write_text(f"{f} v2")
+        assert bench.traffic_record("fwd") is None
+        (csrc / f).write_text(f"{f} v1")
+        assert bench.traffic_record("fwd")["hbm_bytes_per_launch"] == 1.0
     (csrc / "fwd_kernel.h").write_text("forward v2")
     assert bench.traffic_record("fwd") is None
     assert bench.traffic_record("dec")["hbm_bytes_per_launch"] == 2.0
