@@ -87,10 +87,22 @@ template <int CPR, int DB>
 __device__ __forceinline__ u32x4 tr_operand(const void* tile, const TrOffsets<CPR, DB>& to, int ks2, int db)
 {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)tile +
-                          (uint32_t)(ks2 * 16 * CPR * 16);
-    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[0][db]));
-    const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[1][db]));
+    typedef __attribute__((address_space(3))) char lds_char;
+    i16x4 t1, t2;
+    if constexpr (CPR >= 16) {
+        // d = 128: addresses formed as integers (the pointer form below made
+        // the compiler spill at 256 registers)
+        const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)tile +
+                              (uint32_t)(ks2 * 16 * CPR * 16);
+        t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[0][db]));
+        t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(base + to.off[1][db]));
+    } else {
+        // d = 64: the tile base and the 16*ks2-row step fold into the
+        // instructions' offset fields (the integer form cost an add per read)
+        lds_char* base = (lds_char*)tile + ks2 * 16 * CPR * 16;
+        t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + to.off[0][db]));
+        t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + to.off[1][db]));
+    }
     const u32x2 w1 = __builtin_bit_cast(u32x2, t1), w2 = __builtin_bit_cast(u32x2, t2);
     return (u32x4){w1[0], w1[1], w2[0], w2[1]};
 }
@@ -242,21 +254,31 @@ bwd_dkdv(BwdParams p)
                 for (int kb = 0; kb < KB; ++kb)
                     s[kb] = TR::mma32(__builtin_bit_cast(v8, qa), __builtin_bit_cast(v8, kw[kb][ks]), s[kb]);
             }
-            // lse2 of the lane's 16 query rows: four 16-byte LDS reads
-            f32x4 l2v[4];
+            // P = exp2(s*c - lse2), lse2 of the lane's 16 query rows read as four
+            // 16-byte LDS vectors.  At d = 128 each is read where its four rows
+            // are used (holding all 16 values, and D's below, spilled registers
+            // there); at d = 64 (one wave per SIMD, registers to spare) all four
+            // are read first, so their latency overlaps.  Every exponential is
+            // formed (rows past the end carry lse2 = +inf and give 0); the empty
+            // asm keeps each one out of a per-element branch.  Pairs that are not
+            // visible are then set to 0, on tiles that are not wholly visible only.
+            constexpr bool LATE = D == 128;
+            f32x4 l2e[LATE ? 1 : 4];
+            if constexpr (!LATE) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) l2v[g4] = *(const f32x4*)&s_l2[buf][32 * h + 8 * g4 + 4 * hh];
-            // P = exp2(s*c - lse2).  Every exponential is formed (rows past the end
-            // carry lse2 = +inf and give 0); the empty asm keeps each one out of a
-            // per-element branch.  Pairs that are not visible are then set to 0,
-            // on tiles that are not wholly visible only.
+                for (int g4 = 0; g4 < 4; ++g4) l2e[g4] = *(const f32x4*)&s_l2[buf][32 * h + 8 * g4 + 4 * hh];
+            }
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 l2v = LATE ? *(const f32x4*)&s_l2[buf][32 * h + 8 * g4 + 4 * hh] : l2e[LATE ? 0 : g4];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2v[j >> 2][j & 3]));
-                    asm volatile("" : "+v"(s[kb][j]));
-                }
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        s[kb][4 * g4 + i] = fast_exp2(fmaf(s[kb][4 * g4 + i], c, -l2v[i]));
+                        asm volatile("" : "+v"(s[kb][4 * g4 + i]));
+                    }
+            }
             const bool all = keys_all_on && qh + 32 <= N && (!p.causal || qh >= k_wave + KW - 1);
             if (!all) {
 #pragma unroll
@@ -292,15 +314,24 @@ bwd_dkdv(BwdParams p)
                 for (int kb = 0; kb < KB; ++kb)
                     dp[kb] = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][kb][ks][lane]), dp[kb]);
             }
-            // D of the same rows, read where it is used
-            f32x4 dsv[4];
+            // dS = P (dP - D), D of the same rows read as four 16-byte vectors
+            // (each where its rows are used at d = 128, all first at d = 64)
+            f32x4 dse[LATE ? 1 : 4];
+            if constexpr (!LATE) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) dsv[g4] = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
+                for (int g4 = 0; g4 < 4; ++g4) dse[g4] = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
+            }
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 dsv = LATE ? *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh] : dse[LATE ? 0 : g4];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dp[kb][4 * g4 + i] = s[kb][4 * g4 + i] * (dp[kb][4 * g4 + i] - dsv[i]);
+            }
             v8 da[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) dp[kb][j] = s[kb][j] * (dp[kb][j] - dsv[j >> 2][j & 3]);
                 da[kb][0] = pack8<T>(dp[kb], 0);
                 da[kb][1] = pack8<T>(dp[kb], 1);
             }
