@@ -477,8 +477,10 @@ struct BlockScan {
         if (t < kt_end) {
             const int k0 = t * BC;            // < N: t < kt_end
             const int kb_lo = k0 / blk, kb_hi = (min(k0 + BC, N) - 1) / blk;
+            // every flag load issued at once (a short-circuit || would issue
+            // them one after another, each waiting for the previous)
             for (int qb = qb_lo; qb <= qb_hi; ++qb)
-                for (int kbl = kb_lo; kbl <= kb_hi; ++kbl) any = any || flags[(size_t)qb * nb + kbl] != 0;
+                for (int kbl = kb_lo; kbl <= kb_hi; ++kbl) any |= flags[(size_t)qb * nb + kbl] != 0;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const int key = k0 + 32 * kb;
@@ -573,10 +575,22 @@ fwd_m32_h16(FwdParams p)
     const int order = p.kv_order;
     auto tile_at = [&](int it) { return order ? (kt_end - 1 - it) : it; };
 
+    // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7].  Block-sparse calls
+    // load it before the flag scan (whose loads it then shares a round trip
+    // with); dense calls after issuing the first K/V copies.
+    u32x4 qw[DK];
+    const int qrow = min(qi, N - 1);
+    auto load_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks)
+            qw[ks] = q_mode16(*(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8), p.qmode);
+    };
+
     // block-sparse: first tile with an attended block (kt_end if none)
     BlockScan<BR, BC> scan;
     int t0 = tile_at(0);
     if constexpr (SPARSE) {
+        load_q();
         scan.init(p, bh, q0, q0 + wave * 32, kt_end);
         t0 = scan.next(0, lane);
     }
@@ -591,13 +605,10 @@ fwd_m32_h16(FwdParams p)
         vplan.issue(sv[0], V, t0 * BC, N, wave);
     }
 
-    // Q^T operand: lane holds Q[qi][16*ks + 8*hh + 0..7].  The empty asm
-    // consumes it here, so the compiler's wait for these loads sits before the
-    // loop and not inside it (where it would also drain the tile prefetches).
-    u32x4 qw[DK];
-    const int qrow = min(qi, N - 1);
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) qw[ks] = q_mode16(*(const u32x4*)(Q + (size_t)qrow * D + ks * 16 + hh * 8), p.qmode);
+    // The empty asm consumes Q here, so the compiler's wait for its loads sits
+    // before the loop and not inside it (where it would also drain the tile
+    // prefetches).
+    if constexpr (!SPARSE) load_q();
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(qw[ks]));
     v8 qf[DK];
