@@ -483,61 +483,69 @@ bwd_dq(BwdParams p)
         // causal: every key of the tile follows every query of the wave
         if (p.causal && k0 > wave_q0 + 31) continue;
 
-        // S^T = K Q^T and dP^T = V dO^T: lane holds query column `col`, key
-        // rows 32*kb + 8*(j/4) + 4*hh + j%4
-        f32x16 s[NKB], dp[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = (f32x16){};
-            dp[kb] = (f32x16){};
-            const int r = kb * 32 + col;
-#pragma unroll
-            for (int ks = 0; ks < DK; ++ks) {
-                const u32x4 ka = sk[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
-                const u32x4 va = sv[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
-                s[kb] = TR::mma32(__builtin_bit_cast(v8, ka), __builtin_bit_cast(v8, qw[ks]), s[kb]);
-                dp[kb] = TR::mma32(__builtin_bit_cast(v8, va), __builtin_bit_cast(v8, gw[ks]), dp[kb]);
-            }
-        }
-        // dS^T = P^T (dP^T - D), P^T = exp2(s*c - lse2), 0 for masked pairs.
-        // Every exponential is formed (a row past the end has lse2 = +inf); the
-        // empty asm keeps each one out of a per-element branch, and the
-        // visibility test runs only on tiles that are not wholly visible.
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2));
-                asm volatile("" : "+v"(s[kb][j]));
-            }
+        // The tile as two 32-key blocks: S^T = K Q^T and dP^T = V dO^T of each
+        // block (lane holds query column `col`, key rows 32*kb + 8*(j/4) +
+        // 4*hh + j%4), then block 0's vector work (dS^T = P^T (dP^T - D),
+        // P^T = exp2(s*c - lse2), 0 for masked pairs) beside block 1's
+        // products, and block 1's vector work beside the first half of
+        // dQ^T += K^T dS^T.  Per element the operations and their order are
+        // unchanged.  Every exponential is formed (a row past the end has
+        // lse2 = +inf); the empty asm keeps each one out of a per-element
+        // branch, and the visibility test runs only on tiles that are not
+        // wholly visible.
         const bool all = !mrow && !pad_any && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
-        if (!all) {
+        {
+            f32x16 s[NKB], dp[NKB];
+            auto products = [&](int kb) __attribute__((always_inline)) {
+                s[kb] = (f32x16){};
+                dp[kb] = (f32x16){};
+                const int r = kb * 32 + col;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                for (int ks = 0; ks < DK; ++ks) {
+                    const u32x4 ka = sk[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
+                    const u32x4 va = sv[buf][r * CPR + swz_kt<CPR>(r, ks * 2 + hh)];
+                    s[kb] = TR::mma32(__builtin_bit_cast(v8, ka), __builtin_bit_cast(v8, qw[ks]), s[kb]);
+                    dp[kb] = TR::mma32(__builtin_bit_cast(v8, va), __builtin_bit_cast(v8, gw[ks]), dp[kb]);
+                }
+            };
+            auto vector = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-                    bool vis = key < N && qi < N;
-                    if (p.causal) vis = vis && key <= qi;
-                    if constexpr (MASKED) vis = vis && ((padw[kb][j >> 2] >> (8 * (j & 3))) & 0xffu) == 0;
-                    if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
-                    s[kb][j] = vis ? s[kb][j] : 0.f;
+                    s[kb][j] = fast_exp2(fmaf(s[kb][j], c, -l2));
+                    asm volatile("" : "+v"(s[kb][j]));
                 }
-            }
-        }
+                if (!all) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+                        bool vis = key < N && qi < N;
+                        if (p.causal) vis = vis && key <= qi;
+                        if constexpr (MASKED) vis = vis && ((padw[kb][j >> 2] >> (8 * (j & 3))) & 0xffu) == 0;
+                        if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
+                        s[kb][j] = vis ? s[kb][j] : 0.f;
+                    }
+                }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s[kb][j] = s[kb][j] * (dp[kb][j] - dsum);
-        // dQ^T += K^T dS^T, contraction over the tile's keys
+                for (int j = 0; j < 16; ++j) s[kb][j] = s[kb][j] * (dp[kb][j] - dsum);
+            };
+            // dQ^T += K^T dS^T over the 16 keys of chunk ks2
+            auto dq_chunk = [&](int ks2) __attribute__((always_inline)) {
+                const v8 da = pack8<T>(s[ks2 >> 1], ks2 & 1);
 #pragma unroll
-        for (int ks2 = 0; ks2 < KS; ++ks2) {
-            const v8 da = pack8<T>(s[ks2 >> 1], ks2 & 1);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x4 ka = tr_operand(sk[buf], tro, ks2, db);
-                dq[db] = TR::mma32(__builtin_bit_cast(v8, ka), da, dq[db]);
-            }
+                for (int db = 0; db < DB; ++db) {
+                    const u32x4 ka = tr_operand(sk[buf], tro, ks2, db);
+                    dq[db] = TR::mma32(__builtin_bit_cast(v8, ka), da, dq[db]);
+                }
+            };
+            static_assert(NKB == 2 && KS == 4, "two 32-key blocks per tile");
+            products(0);
+            products(1);
+            vector(0);
+            dq_chunk(0);
+            dq_chunk(1);
+            vector(1);
+            dq_chunk(2);
+            dq_chunk(3);
         }
     }
 
