@@ -219,8 +219,16 @@ inline int64_t fwd_grid(const FwdPlan& p)
 // pipeline (unless generic_loop asks for the compiler-scheduled loop).
 inline bool fwd_pipelined(const FwdPlan& p)
 {
+#ifdef ATTN_LDS_POISON
+    // the LDS-poisoning debug build checks the copies the C++ loops issue; the
+    // pipeline issues its own (its waits are checked by bitwise equality with
+    // the C++ loop)
+    (void)p;
+    return false;
+#else
     return p.dtype != ATTN_F32 && !p.sparse && !p.mask && p.d == 128 && p.br == 256 && p.bc == 64 &&
            !p.generic && p.order == 0 && p.slack == 0;
+#endif
 }
 
 // Persistent grid (pipelined instance only): one workgroup per compute unit

@@ -407,6 +407,21 @@ struct TilePlan {
     {
         const uint64_t gb = uniform_ptr(g + (size_t)k0 * (CPR * 8));
         const uint32_t lb = lds_addr(lds_tile);
+#ifdef ATTN_LDS_POISON
+        // Debug build: NaN into exactly the slots these copies fill, written
+        // after the wait that freed them and before the copies are issued.  A
+        // read that is not ordered after the copies' completion (a missing
+        // wait or barrier) then sees NaN instead of the previous tile's data.
+        {
+            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+            const uint32_t lane = (uint32_t)(threadIdx.x & 63);
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                *(lds_u32x4*)(uintptr_t)(lb + (uint32_t)(((wave * NI + i) * 64) * 16) + lane * 16u) =
+                    (u32x4){0x7fc00000u, 0x7fc00000u, 0x7fc00000u, 0x7fc00000u};
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+#endif
         if (k0 + BC <= N) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) lds_dma16<NT>(gb, off[i], lb + (uint32_t)((wave * NI + i) * 64 * 16));
