@@ -10,7 +10,8 @@ would read NaN instead of the previous tile's finite data and fail here.
 
 Each library runs in a child process of its own; the cases cover the 16-bit
 forward (plain, causal, ragged, padded, both fold orders), the fp32 forward,
-the block-sparse walk, the cache path and the gradient.
+the block-sparse walk, the cache path and the gradient (whose pipelined dQ
+loop in the release build is thereby checked bitwise against the C++ loop).
 """
 import os
 import subprocess
@@ -74,12 +75,15 @@ qd = q[:, :, :3].contiguous()
 put("decode_bf16_d128", *A.decode_fwd(qd, k, v, scale=128 ** -0.5, causal=True))
 dmask = (torch.arange(1000, device=dev) > 700).to(torch.uint8)[None].repeat(2, 1).contiguous()
 put("decode_bf16_d128_mask", *A.decode_fwd(qd, k, v, scale=128 ** -0.5, causal=True, key_padding_mask=dmask))
-for d in (128, 64):
-    q, k, v = t(1, 2, 500, d, bf, 7 + d)
-    o, lse = A.fwd(q, k, v, scale=d ** -0.5, causal=True, generic_loop=True)
+# the release build's dQ kernel runs its full key tiles through its software
+# pipeline at d = 128, the poisoned build through the C++ loop
+for d, N, causal, dt, name in ((128, 500, True, bf, "bf16"), (64, 500, True, bf, "bf16"),
+                               (128, 2048, False, f16, "f16"), (128, 1536, True, bf, "bf16")):
+    q, k, v = t(1, 2, N, d, dt, 7 + d + N)
+    o, lse = A.fwd(q, k, v, scale=d ** -0.5, causal=causal, generic_loop=True)
     g = torch.Generator(device="cpu").manual_seed(9)
-    do = torch.randn(1, 2, 500, d, generator=g).to(bf).to(dev)
-    put(f"bwd_bf16_d{d}", *A.bwd(q, k, v, o, do, lse, scale=d ** -0.5, causal=True))
+    do = torch.randn(1, 2, N, d, generator=g).to(dt).to(dev)
+    put(f"bwd_{name}_d{d}_N{N}_c{int(causal)}", *A.bwd(q, k, v, o, do, lse, scale=d ** -0.5, causal=causal))
 np.savez(out, **res)
 print("done", flush=True)
 """
@@ -109,6 +113,8 @@ def test_poisoned_build_matches_release_bitwise(tmp_path):
     # pipelines: the switch was compiled in
     lines = [l for l in r.stderr.splitlines() if l.startswith("attn: attn_fwd kernel=fwd_m32_h16<bf16,d128,256x64>")]
     assert len(lines) >= 4 and all("loop=generic" in l for l in lines), "\n".join(lines)
+    bl = [l for l in r.stderr.splitlines() if l.startswith("attn: attn_bwd ")]
+    assert len(bl) == 4 and all("dq_loop=generic" in l for l in bl), "\n".join(bl)
     a, b = np.load(tmp_path / "rel.npz"), np.load(tmp_path / "poi.npz")
     assert sorted(a.files) == sorted(b.files)
     for name in sorted(a.files):

@@ -445,6 +445,22 @@ inline int plan_decode(const void* q, const void* k, const void* v, const void* 
 }
 
 // ---------------------------------------------------------------- backward
+// The dQ kernel of the 16-bit d = 128 gradient without a key-padding mask
+// runs the key tiles every row of a workgroup sees in full through its
+// software pipeline.
+inline bool bwd_dq_pipelined(int d, bool mask)
+{
+#ifdef ATTN_LDS_POISON
+    // the poisoned build checks the C++ loop's copies; the pipeline's waits
+    // are checked by bitwise equality with that loop
+    (void)d;
+    (void)mask;
+    return false;
+#else
+    return d == 128 && !mask;
+#endif
+}
+
 inline size_t bwd_ws_bytes(int B, int H, int N)
 {
     if (B <= 0 || H <= 0 || N <= 0) return 0;
@@ -549,10 +565,10 @@ inline int trace_decode_line(char* buf, size_t n, const char* entry, const DecPl
 }
 
 inline int trace_plain_line(char* buf, size_t n, const char* entry, const char* kernels, int dtype, int B, int H,
-                            int N, int d, int causal, int mask, size_t ws)
+                            int N, int d, int causal, int mask, size_t ws, const char* tail = "")
 {
-    return snprintf(buf, n, "attn: %s kernel=%s<%s,d%d> B=%d H=%d N=%d causal=%d mask=%d workspace=%zu\n", entry,
-                    kernels, dtype_name(dtype), d, B, H, N, causal ? 1 : 0, mask, ws);
+    return snprintf(buf, n, "attn: %s kernel=%s<%s,d%d> B=%d H=%d N=%d causal=%d mask=%d workspace=%zu%s\n", entry,
+                    kernels, dtype_name(dtype), d, B, H, N, causal ? 1 : 0, mask, ws, tail);
 }
 
 inline int trace_status_line(char* buf, size_t n, const char* entry, int st)

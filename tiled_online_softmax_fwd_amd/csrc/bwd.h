@@ -22,6 +22,7 @@ struct BwdParams {
     float scale;            // natural-log factor of q.k
     float c;                // scale * log2(e)
     int causal;
+    int pipe;               // 1: bwd_dq runs its full key tiles through bwd_dq_pipe_asm.h
 };
 
 typedef hipError_t (*BwdLaunchFn)(const BwdParams&, hipStream_t);

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include "bwd.h"
 #include "fwd_kernel.h"
+#include "bwd_dq_pipe_asm.h"
 
 
 namespace attnk {
@@ -384,8 +385,15 @@ bwd_dq(BwdParams p)
     // K tiles are read row-wise and transposed, V tiles row-wise: both use
     // swz_kt, so one copy plan serves both
     using Plan = TilePlan<BC, CPR, NW, 3>;
-    __shared__ u32x4 sk[2][BC * CPR];
-    __shared__ u32x4 sv[2][BC * CPR];
+    // 16-bit d = 128 without a key-padding mask: the key tiles every row of
+    // the workgroup sees in full run through the software pipeline of
+    // bwd_dq_pipe_asm.h first
+    constexpr bool PIPE = !MASKED && D == 128 && NW == 8;
+    // K buffers kv[0..1], V buffers kv[2..3]: one array, so that the pipeline
+    // addresses all of them from one base
+    __shared__ u32x4 kv[4][BC * CPR];
+    u32x4 (*const sk)[BC * CPR] = kv;
+    u32x4 (*const sv)[BC * CPR] = kv + 2;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -448,17 +456,73 @@ bwd_dq(BwdParams p)
 
     const int nkt = (N + BC - 1) / BC;
     const int kt_end = p.causal ? min(nkt, (min(q0 + 32 * NW, N) - 1) / BC + 1) : nkt;
+    const float c = p.c;
+    int kt_first = 0;
+    if constexpr (PIPE) {
+        // The pipeline takes 32-key tiles 0 .. n32-1 (n32 even, every key
+        // visible to every query of the workgroup, no tile past N) and leaves
+        // dq updated; the loop below resumes at 64-key tile n32/2.  dO^T is
+        // read from per-wave LDS slots inside it.
+        __shared__ u32x4 s_gw[NW][DK][64];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) s_gw[wave][ks][lane] = gw[ks];
+        int n32 = p.causal ? q0 / 32 : N / 32;
+        n32 = min(n32, N / 32) & ~1;
+        if (p.pipe && n32 >= 2) {
+            // the block's addresses come from an opaque copy of the lane: the
+            // loop below computes its own after the block instead of keeping
+            // shared values live across it
+            int pl = lane;
+            asm volatile("" : "+v"(pl));
+            using P32 = TilePlan<32, CPR, NW, 3>;
+            static_assert(P32::NI == 1, "one copy instruction per wave per 32-key tile");
+            P32 p32;
+            p32.init(wave, pl);
+            p32.issue(kv[0], K, 0, N, wave);
+            p32.issue(kv[2], V, 0, N, wave);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const uint32_t lb = lds_addr(kv[0]);
+            const int pcol = pl & 31, phh = pl >> 5;
+            uint32_t ka[DK], tr[8];
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) ka[ks] = lb + (uint32_t)(pcol * CPR + swz_kt<CPR>(pcol, 2 * ks + phh)) * 16u;
+            {
+                TrOffsets<CPR, DB> t0;
+                t0.init(pl);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) tr[4 * t + db] = lb + t0.off[t][db];
+            }
+            const uint32_t gwaddr = lds_addr(&s_gw[wave][0][pl]);
+            uint32_t offa = p32.off[0] + 32 * CPR * 16, offb = p32.off[0];
+            const uint32_t kdst = __builtin_amdgcn_readfirstlane(lb + (uint32_t)(wave * 1024));
+            const uint64_t kbase = uniform_ptr(K), vbase = uniform_ptr(V);
+            uint32_t pairs = __builtin_amdgcn_readfirstlane((uint32_t)(n32 - 2) / 2);
+            uint32_t m0save;
+            if constexpr (std::is_same<T, __bf16>::value)
+                asm volatile(ATTN_DQ_PIPE_ASM_BF16 ATTN_DQ_PIPE_OPERANDS);
+            else
+                asm volatile(ATTN_DQ_PIPE_ASM_F16 ATTN_DQ_PIPE_OPERANDS);
+            kt_first = n32 / 2;
+            __syncthreads();    // every wave is done with the buffers the loop refills
+        }
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) gw[ks] = s_gw[wave][ks][lane];
+    }
+    // the plans are built after the block (not kept live across it)
+    int wv = wave;
+    asm volatile("" : "+s"(wv));
     Plan plan;
-    plan.init(wave, lane);
+    plan.init(wv, lane);
     TrOffsets<CPR, DB> tro;
     tro.init(lane);
-    const float c = p.c;
-    if (kt_end > 0) {
-        plan.issue(sk[0], K, 0, N, wave);
-        plan.issue(sv[0], V, 0, N, wave);
-        if constexpr (MASKED) load_pad(0);
+    if (kt_first < kt_end) {
+        plan.issue(sk[kt_first & 1], K, kt_first * BC, N, wave);
+        plan.issue(sv[kt_first & 1], V, kt_first * BC, N, wave);
+        if constexpr (MASKED) load_pad(kt_first * BC);
     }
-    for (int kt = 0; kt < kt_end; ++kt) {
+    for (int kt = kt_first; kt < kt_end; ++kt) {
         const int buf = kt & 1;
         const int k0 = kt * BC;
         wait_vmcnt<0>();
