@@ -10,8 +10,8 @@ would read NaN instead of the previous tile's finite data and fail here.
 
 Each library runs in a child process of its own; the cases cover the 16-bit
 forward (plain, causal, ragged, padded, both fold orders), the fp32 forward,
-the block-sparse walk, the cache path and the gradient (whose pipelined dQ
-loop in the release build is thereby checked bitwise against the C++ loop).
+the block-sparse walk, the cache path and the gradient (whose pipelined loops
+in the release build are thereby checked bitwise against the C++ loops).
 """
 import os
 import subprocess
@@ -75,8 +75,8 @@ qd = q[:, :, :3].contiguous()
 put("decode_bf16_d128", *A.decode_fwd(qd, k, v, scale=128 ** -0.5, causal=True))
 dmask = (torch.arange(1000, device=dev) > 700).to(torch.uint8)[None].repeat(2, 1).contiguous()
 put("decode_bf16_d128_mask", *A.decode_fwd(qd, k, v, scale=128 ** -0.5, causal=True, key_padding_mask=dmask))
-# the release build's dQ kernel runs its full key tiles through its software
-# pipeline at d = 128, the poisoned build through the C++ loop
+# the release build's dK/dV and dQ kernels run their full tiles through their
+# software pipelines at d = 128, the poisoned build through the C++ loops
 for d, N, causal, dt, name in ((128, 500, True, bf, "bf16"), (64, 500, True, bf, "bf16"),
                                (128, 2048, False, f16, "f16"), (128, 1536, True, bf, "bf16")):
     q, k, v = t(1, 2, N, d, dt, 7 + d + N)
@@ -114,7 +114,7 @@ def test_poisoned_build_matches_release_bitwise(tmp_path):
     lines = [l for l in r.stderr.splitlines() if l.startswith("attn: attn_fwd kernel=fwd_m32_h16<bf16,d128,256x64>")]
     assert len(lines) >= 4 and all("loop=generic" in l for l in lines), "\n".join(lines)
     bl = [l for l in r.stderr.splitlines() if l.startswith("attn: attn_bwd ")]
-    assert len(bl) == 4 and all("dq_loop=generic" in l for l in bl), "\n".join(bl)
+    assert len(bl) == 4 and all("loops=generic" in l for l in bl), "\n".join(bl)
     a, b = np.load(tmp_path / "rel.npz"), np.load(tmp_path / "poi.npz")
     assert sorted(a.files) == sorted(b.files)
     for name in sorted(a.files):

@@ -69,4 +69,4 @@ def test_trace_names_the_launched_kernels():
     assert "attn_decode_fwd kernel=dec_split+dec_merge<bf16,d128> B=1 H=8 Nq=1 Nk=1024" in dec
     assert "attn_naive_fwd kernel=gemm_simt+row_softmax+gemm_simt<f32,d64>" in naive
     assert "attn_fwd kernel=fwd_m32_h16<bf16,d128,256x64> B=1 H=8 N=1024" in fwd2
-    assert "attn_bwd kernel=bwd_pre+bwd_dkdv+bwd_dq<bf16,d128>" in bwd and "dq_loop=pipelined" in bwd
+    assert "attn_bwd kernel=bwd_pre+bwd_dkdv+bwd_dq<bf16,d128>" in bwd and "loops=pipelined" in bwd

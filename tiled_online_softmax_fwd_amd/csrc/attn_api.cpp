@@ -283,12 +283,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     p.scale = scale;
     p.c = attnh::log2e_factor(scale);
     p.causal = causal ? 1 : 0;
-    p.pipe = attnh::bwd_dq_pipelined(d, key_padding_mask != nullptr) ? 1 : 0;
+    p.pipe = attnh::bwd_pipelined(d, key_padding_mask != nullptr, B, H, N) ? 1 : 0;
     if (attnh::trace_on()) {
         char line[768];
         attnh::trace_plain_line(line, sizeof(line), "attn_bwd", "bwd_pre+bwd_dkdv+bwd_dq", dtype, B, H, N, d, causal,
                                 key_padding_mask ? 1 : 0, attnh::bwd_ws_bytes(B, H, N),
-                                p.pipe ? " dq_loop=pipelined" : " dq_loop=generic");
+                                p.pipe ? " loops=pipelined" : " loops=generic");
         attnh::trace_emit(line);
     }
     const hipError_t e = attnk::lookup_bwd(dtype == ATTN_BF16 ? 0 : 1, d)(p, (hipStream_t)stream);

@@ -445,19 +445,24 @@ inline int plan_decode(const void* q, const void* k, const void* v, const void* 
 }
 
 // ---------------------------------------------------------------- backward
-// The dQ kernel of the 16-bit d = 128 gradient without a key-padding mask
-// runs the key tiles every row of a workgroup sees in full through its
-// software pipeline.
-inline bool bwd_dq_pipelined(int d, bool mask)
+// The dK/dV and dQ kernels of the 16-bit d = 128 gradient without a
+// key-padding mask run their full tiles through their software pipelines.
+// Those address a head's rows and its lse2 (from its D, in the same
+// workspace) with 32-bit byte offsets, which the sizes must allow.
+inline bool bwd_pipelined(int d, bool mask, int B, int H, int N)
 {
 #ifdef ATTN_LDS_POISON
-    // the poisoned build checks the C++ loop's copies; the pipeline's waits
-    // are checked by bitwise equality with that loop
+    // the poisoned build checks the C++ loops' copies; the pipelines' waits
+    // are checked by bitwise equality with those loops
     (void)d;
     (void)mask;
+    (void)B;
+    (void)H;
+    (void)N;
     return false;
 #else
-    return d == 128 && !mask;
+    const uint64_t rows = (uint64_t)B * H * N;
+    return d == 128 && !mask && (uint64_t)N * 256u <= 0xffffffffull && 4u * rows + 4u * (uint64_t)N <= 0xffffffffull;
 #endif
 }
 

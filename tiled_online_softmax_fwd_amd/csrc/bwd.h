@@ -22,7 +22,7 @@ struct BwdParams {
     float scale;            // natural-log factor of q.k
     float c;                // scale * log2(e)
     int causal;
-    int pipe;               // 1: bwd_dq runs its full key tiles through bwd_dq_pipe_asm.h
+    int pipe;               // 1: bwd_dkdv and bwd_dq run their full tiles through their pipelines
 };
 
 typedef hipError_t (*BwdLaunchFn)(const BwdParams&, hipStream_t);

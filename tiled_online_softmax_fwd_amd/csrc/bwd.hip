@@ -28,6 +28,7 @@
 #include "bwd.h"
 #include "fwd_kernel.h"
 #include "bwd_dq_pipe_asm.h"
+#include "bwd_dkdv_pipe_asm.h"
 
 
 namespace attnk {
@@ -108,6 +109,20 @@ __device__ __forceinline__ u32x4 tr_operand(const void* tile, const TrOffsets<CP
     return (u32x4){w1[0], w1[1], w2[0], w2[1]};
 }
 
+// One 4-byte global load per lane straight into LDS (lane i writes bytes
+// lds_base + 4i .. +3); completion counts in vmcnt like the 16-byte form.
+__device__ __forceinline__ void lds_dma4(uint64_t gbase, uint32_t voff, uint32_t lds_base)
+{
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %3\n\t"
+                 "global_load_lds_dword %1, %2\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(voff), "s"(gbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+
 // Round the 8 accumulator values of chunk ks2 (elements 8*ks2 .. 8*ks2+7) to T.
 template <typename T>
 __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
@@ -132,8 +147,15 @@ bwd_dkdv(BwdParams p)
     using v8 = typename TR::v8;
     constexpr int CPR = D * 2 / 16, DK = D / 16, DB = D / 32, BQ = 64, NH = BQ / 32, KW = 32 * KB;
     using Plan = TilePlan<BQ, CPR, NW, 3>;
-    __shared__ u32x4 sq[2][BQ * CPR];
-    __shared__ u32x4 sg[2][BQ * CPR];
+    // 16-bit d = 128 without a key-padding mask, 32 keys per wave: the query
+    // tiles whose rows see every key of the workgroup run through the software
+    // pipeline of bwd_dkdv_pipe_asm.h
+    constexpr bool PIPE = !MASKED && D == 128 && NW == 8 && KB == 1;
+    // Q buffers sqg[0..1], dO buffers sqg[2..3]: one array, which the pipeline
+    // also uses (with its own layouts)
+    __shared__ u32x4 sqg[4][BQ * CPR];
+    u32x4 (*const sq)[BQ * CPR] = sqg;
+    u32x4 (*const sg)[BQ * CPR] = sqg + 2;
     __shared__ u32x4 s_vw[NW][KB][DK][64];   // each wave's V^T operands (registers are short)
     __shared__ __attribute__((aligned(16))) float s_l2[2][BQ];
     __shared__ __attribute__((aligned(16))) float s_d[2][BQ];
@@ -195,16 +217,8 @@ bwd_dkdv(BwdParams p)
     const int k_wg = kt * KW * NW;
     const int qt0 = p.causal ? k_wg / BQ : 0;
     const int nqt = (N + BQ - 1) / BQ;
-    Plan plan;
-    plan.init(wave, lane);
-    TrOffsets<CPR, DB> tro;
-    tro.init(lane);
     const float c = p.c;
 
-    auto stage = [&](int buf, int qt) __attribute__((always_inline)) {
-        plan.issue(sq[buf], Q, qt * BQ, N, wave);
-        plan.issue(sg[buf], G, qt * BQ, N, wave);
-    };
     // lse2 and D of a query tile: loaded into registers one tile ahead by the
     // first BQ threads, stored to LDS at the top of the tile's step
     float nl2 = 0.f, nd = 0.f;
@@ -214,13 +228,89 @@ bwd_dkdv(BwdParams p)
         nl2 = qi < N ? L2[qr] : INFINITY;
         nd = DS[qr];
     };
-    if (qt0 < nqt) {
-        stage(0, qt0);
-        if (threadIdx.x < BQ) row_terms(qt0);
+    // Query tiles in the order qa .. nqt-1, then qt0 .. qa-1: under causal
+    // masking the tiles that cross the workgroup's keys come last (qa is the
+    // first tile whose rows all follow every key of the workgroup), so that
+    // the pipelined block below can take a leading run of full tiles and this
+    // loop the rest, in one order for every path.
+    const int qa = p.causal ? min(qt0 + KW * NW / BQ, nqt) : 0;
+    int q_first = qa;
+    if constexpr (PIPE) {
+        // Tiles qa .. qb-1 through the block: all 64 rows lie before N and
+        // every key of the workgroup lies before N.  The block takes them as
+        // 32-row steps and leaves dk and dv updated.
+        const int qb = N / BQ;
+        if (p.pipe && k_wg + KW * NW <= N && qb > qa) {
+            __shared__ __attribute__((aligned(16))) float s_ld[NW][2][64];   // lse2 and D per step, per wave
+            constexpr uint32_t TILE = 32 * CPR * 16, ROWQ = 0, ROWG = 2 * TILE;
+            const int qs = qa * BQ;
+            int pl = lane;
+            asm volatile("" : "+v"(pl));
+            const int phh = pl >> 5, pr = pl & 31;
+            // row-operand layout: the copy of wave w puts, at lane (r, hh) of
+            // its 1024 bytes, row r's 16-byte chunk 2w + hh (the operand of
+            // lane (r, hh) for ks = w)
+            uint32_t offr = (uint32_t)(qs + pr) * (CPR * 16u) + (uint32_t)(2 * wave + phh) * 16u;
+            // transposing-read layout: 512-byte block b = (tt*4 + db)*2 + u
+            // holds, at 16-byte slot k, row 16 tt + 8 u + 4 (k/16) + (k/2)%4,
+            // chunk 4 db + 2 ((k/8)%2) + k%2 (lanes 2k, 2k+1 read its halves)
+            const int blk = 2 * wave + phh;
+            const int trow = 16 * (blk >> 3) + 8 * (blk & 1) + 4 * (pr >> 4) + ((pr >> 1) & 3);
+            const int tch = 4 * ((blk >> 1) & 3) + 2 * ((pr >> 3) & 1) + (pr & 1);
+            uint32_t offt = (uint32_t)(qs + trow) * (CPR * 16u) + (uint32_t)tch * 16u;
+            // lse2 (lanes 0..31) and D (lanes 32..63) of the step's rows,
+            // addressed from the head's D (the host checks the distance fits)
+            const uint32_t dl = (uint32_t)((const char*)p.lse2 - (const char*)p.dsum);
+            uint32_t offl = pl < 32 ? dl + (uint32_t)(qs + pl) * 4u : (uint32_t)(qs + pl - 32) * 4u;
+            const uint64_t qbase = uniform_ptr(Q), gbase = uniform_ptr(G), dbase = uniform_ptr(DS);
+            const uint32_t lb = lds_addr(sqg[0]), ldb = lds_addr(&s_ld[0][0][0]);
+            lds_dma16(qbase, offr, lb + ROWQ + (uint32_t)wave * 1024u);
+            lds_dma16(gbase, offr, lb + ROWG + (uint32_t)wave * 1024u);
+            lds_dma4(dbase, offl, ldb + (uint32_t)wave * 512u);
+            offr += TILE;
+            offl += 128u;
+            const uint32_t ka = lb + (uint32_t)pl * 16u, tra = lb + (uint32_t)pl * 8u;
+            const uint32_t vwa = lds_addr(&s_vw[wave][0][0][pl]);
+            const uint32_t lda = ldb + (uint32_t)wave * 512u + (uint32_t)phh * 16u;
+            const uint32_t kdst = __builtin_amdgcn_readfirstlane(lb + (uint32_t)wave * 1024u);
+            const uint32_t ldst = __builtin_amdgcn_readfirstlane(ldb + (uint32_t)wave * 512u);
+            uint32_t pairs = __builtin_amdgcn_readfirstlane((uint32_t)(qb - qa - 1));   // (steps - 2) / 2
+            uint32_t m0save;
+            f32x16 (&dk0)[DB] = dk[0];
+            f32x16 (&dv0)[DB] = dv[0];
+            u32x4 (&kw0)[DK] = kw[0];
+            if constexpr (std::is_same<T, __bf16>::value)
+                asm volatile(ATTN_DKDV_PIPE_ASM_BF16 ATTN_DKDV_PIPE_OPERANDS);
+            else
+                asm volatile(ATTN_DKDV_PIPE_ASM_F16 ATTN_DKDV_PIPE_OPERANDS);
+            __syncthreads();    // every wave is done with the block's buffers
+            q_first = qb;
+        }
+    }
+    // the loop's share: tiles q_first .. nqt-1, then qt0 .. qa-1
+    const int n_tail = nqt - q_first, cnt = n_tail + (qa - qt0);
+    auto tile_at = [&](int i) __attribute__((always_inline)) { return i < n_tail ? q_first + i : qt0 + (i - n_tail); };
+    // the copy plans are built after the block (not kept live across it):
+    // opaque copies of the wave and lane stop the compiler from reusing values
+    // computed before it
+    int wv = wave, ln = lane;
+    if constexpr (PIPE) asm volatile("" : "+s"(wv), "+v"(ln));
+    Plan plan;
+    plan.init(wv, ln);
+    TrOffsets<CPR, DB> tro;
+    tro.init(ln);
+    auto stage = [&](int buf, int qt) __attribute__((always_inline)) {
+        plan.issue(sq[buf], Q, qt * BQ, N, wave);
+        plan.issue(sg[buf], G, qt * BQ, N, wave);
+    };
+    if (cnt > 0) {
+        stage(0, tile_at(0));
+        if (threadIdx.x < BQ) row_terms(tile_at(0));
     }
 
-    for (int qt = qt0; qt < nqt; ++qt) {
-        const int buf = (qt - qt0) & 1;
+    for (int i = 0; i < cnt; ++i) {
+        const int qt = tile_at(i);
+        const int buf = i & 1;
         const int q0 = qt * BQ;
         // tile qt landed; every wave is done with tile qt-1 (other buffer)
         if (threadIdx.x < BQ) {
@@ -229,9 +319,9 @@ bwd_dkdv(BwdParams p)
         }
         wait_vmcnt<0>();
         __syncthreads();
-        if (qt + 1 < nqt) {
-            stage(buf ^ 1, qt + 1);
-            if (threadIdx.x < BQ) row_terms(qt + 1);
+        if (i + 1 < cnt) {
+            stage(buf ^ 1, tile_at(i + 1));
+            if (threadIdx.x < BQ) row_terms(tile_at(i + 1));
         }
 
         if (keys_all_off) continue;
