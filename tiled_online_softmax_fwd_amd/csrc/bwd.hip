@@ -123,6 +123,31 @@ __device__ __forceinline__ void lds_dma4(uint64_t gbase, uint32_t voff, uint32_t
                  : "memory");
 }
 
+// Operand-ordered layouts of a 32-row tile with 256-byte rows (d = 128,
+// 16-bit), used by the pipelined blocks: each read instruction of a wave takes
+// one contiguous run, so one address register and the instruction's offset
+// field serve every read, without bank conflicts.  The copy instruction of
+// wave w fills bytes 1024 w .. 1024 w + 1023 of the tile; these give the byte
+// offset, within the tile's rows in memory, of the 16-byte chunk that lane
+// `lane` brings.
+// Row operands: lane (r, hh) of the run for ks holds row r's chunk 2 ks + hh,
+// the operand of lane (r, hh) (run ks = the copy of wave ks).
+__device__ __forceinline__ uint32_t row_layout_src(int wave, int lane)
+{
+    return (uint32_t)(lane & 31) * 256u + (uint32_t)(2 * wave + (lane >> 5)) * 16u;
+}
+// Transposing reads: 512-byte run b = (tt*4 + db)*2 + u holds, at 16-byte slot
+// k, row 16 tt + 8 u + 4 (k/16) + (k/2)%4 and chunk 4 db + 2 ((k/8)%2) + k%2,
+// whose two 8-byte halves lanes 2k and 2k+1 read (the rows 16 tt + 4 hh +
+// {0..3} (u = 0) or {8..11} (u = 1) of column block db).
+__device__ __forceinline__ uint32_t tr_layout_src(int wave, int lane)
+{
+    const int b = 2 * wave + (lane >> 5), k = lane & 31;
+    const int row = 16 * (b >> 3) + 8 * (b & 1) + 4 * (k >> 4) + ((k >> 1) & 3);
+    const int chunk = 4 * ((b >> 1) & 3) + 2 * ((k >> 3) & 1) + (k & 1);
+    return (uint32_t)row * 256u + (uint32_t)chunk * 16u;
+}
+
 // Round the 8 accumulator values of chunk ks2 (elements 8*ks2 .. 8*ks2+7) to T.
 template <typename T>
 __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
@@ -246,18 +271,9 @@ bwd_dkdv(BwdParams p)
             const int qs = qa * BQ;
             int pl = lane;
             asm volatile("" : "+v"(pl));
-            const int phh = pl >> 5, pr = pl & 31;
-            // row-operand layout: the copy of wave w puts, at lane (r, hh) of
-            // its 1024 bytes, row r's 16-byte chunk 2w + hh (the operand of
-            // lane (r, hh) for ks = w)
-            uint32_t offr = (uint32_t)(qs + pr) * (CPR * 16u) + (uint32_t)(2 * wave + phh) * 16u;
-            // transposing-read layout: 512-byte block b = (tt*4 + db)*2 + u
-            // holds, at 16-byte slot k, row 16 tt + 8 u + 4 (k/16) + (k/2)%4,
-            // chunk 4 db + 2 ((k/8)%2) + k%2 (lanes 2k, 2k+1 read its halves)
-            const int blk = 2 * wave + phh;
-            const int trow = 16 * (blk >> 3) + 8 * (blk & 1) + 4 * (pr >> 4) + ((pr >> 1) & 3);
-            const int tch = 4 * ((blk >> 1) & 3) + 2 * ((pr >> 3) & 1) + (pr & 1);
-            uint32_t offt = (uint32_t)(qs + trow) * (CPR * 16u) + (uint32_t)tch * 16u;
+            const int phh = pl >> 5;
+            uint32_t offr = (uint32_t)qs * 256u + row_layout_src(wave, pl);
+            uint32_t offt = (uint32_t)qs * 256u + tr_layout_src(wave, pl);
             // lse2 (lanes 0..31) and D (lanes 32..63) of the step's rows,
             // addressed from the head's D (the host checks the distance fits)
             const uint32_t dl = (uint32_t)((const char*)p.lse2 - (const char*)p.dsum);
@@ -551,43 +567,26 @@ bwd_dq(BwdParams p)
     if constexpr (PIPE) {
         // The pipeline takes 32-key tiles 0 .. n32-1 (n32 even, every key
         // visible to every query of the workgroup, no tile past N) and leaves
-        // dq updated; the loop below resumes at 64-key tile n32/2.  dO^T is
-        // read from per-wave LDS slots inside it.
-        __shared__ u32x4 s_gw[NW][DK][64];
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) s_gw[wave][ks][lane] = gw[ks];
+        // dq updated; the loop below resumes at 64-key tile n32/2.
         int n32 = p.causal ? q0 / 32 : N / 32;
         n32 = min(n32, N / 32) & ~1;
         if (p.pipe && n32 >= 2) {
+            static_assert(CPR * 16 == 256, "256-byte rows");
+            constexpr uint32_t TILE = 32 * 256, ROWS_V = 4 * TILE;
             // the block's addresses come from an opaque copy of the lane: the
             // loop below computes its own after the block instead of keeping
             // shared values live across it
             int pl = lane;
             asm volatile("" : "+v"(pl));
-            using P32 = TilePlan<32, CPR, NW, 3>;
-            static_assert(P32::NI == 1, "one copy instruction per wave per 32-key tile");
-            P32 p32;
-            p32.init(wave, pl);
-            p32.issue(kv[0], K, 0, N, wave);
-            p32.issue(kv[2], V, 0, N, wave);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const uint32_t lb = lds_addr(kv[0]);
-            const int pcol = pl & 31, phh = pl >> 5;
-            uint32_t ka[DK], tr[8];
-#pragma unroll
-            for (int ks = 0; ks < DK; ++ks) ka[ks] = lb + (uint32_t)(pcol * CPR + swz_kt<CPR>(pcol, 2 * ks + phh)) * 16u;
-            {
-                TrOffsets<CPR, DB> t0;
-                t0.init(pl);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) tr[4 * t + db] = lb + t0.off[t][db];
-            }
-            const uint32_t gwaddr = lds_addr(&s_gw[wave][0][pl]);
-            uint32_t offa = p32.off[0] + 32 * CPR * 16, offb = p32.off[0];
-            const uint32_t kdst = __builtin_amdgcn_readfirstlane(lb + (uint32_t)(wave * 1024));
+            uint32_t offa = row_layout_src(wave, pl), offb = tr_layout_src(wave, pl);
             const uint64_t kbase = uniform_ptr(K), vbase = uniform_ptr(V);
+            const uint32_t lb = lds_addr(kv[0]);
+            // rows of tile 0 (K and V); the block copies the rest
+            lds_dma16(kbase, offa, lb + (uint32_t)wave * 1024u);
+            lds_dma16(vbase, offa, lb + ROWS_V + (uint32_t)wave * 1024u);
+            offa += TILE;
+            const uint32_t ka = lb + (uint32_t)pl * 16u, tra = lb + (uint32_t)pl * 8u;
+            const uint32_t kdst = __builtin_amdgcn_readfirstlane(lb + (uint32_t)(wave * 1024));
             uint32_t pairs = __builtin_amdgcn_readfirstlane((uint32_t)(n32 - 2) / 2);
             uint32_t m0save;
             if constexpr (std::is_same<T, __bf16>::value)
@@ -597,8 +596,6 @@ bwd_dq(BwdParams p)
             kt_first = n32 / 2;
             __syncthreads();    // every wave is done with the buffers the loop refills
         }
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) gw[ks] = s_gw[wave][ks][lane];
     }
     // the plans are built after the block (not kept live across it)
     int wv = wave;

@@ -18,8 +18,11 @@ twice, once for the row reads of the score products and once for the
 transposed reads of the dQ products, so that each buffer is in use for one
 iteration only and every buffer, like the two register sets of scores,
 alternates with period 2.  Iteration t copies K and V of tile t+2 (row
-buffers) and K of tile t+1 (transposed-read buffer).  The dO^T operands are
-read from per-wave LDS slots (registers are short).
+buffers) and K of tile t+1 (transposed-read buffer).  The LDS layouts are
+operand-ordered: each read instruction reads one contiguous run (1024 bytes
+for a row operand, 512 for a transposing read), so one address register per
+kind serves every read through the instruction's offset field, and no read
+has a bank conflict.  Q^T and dO^T stay in registers.
 
 Run: python gen_bwd_dq_pipe.py  (rewrites bwd_dq_pipe_asm.h beside this file).
 """
@@ -32,26 +35,24 @@ from gen_fwd_pipe import Emitter, Op, rng, spread  # noqa: E402
 # ---------------------------------------------------------------- register map
 DQ = 0                          # v[0:63]    dQ^T accumulators, dq[db] = v[16db : 16db+15]
 QW = 64                         # v[64:95]   Q^T operand, qw[ks] = v[64+4ks : +3]
-SETS = ((96, 112), (128, 144))  # (S^T / P / dS, dP^T) of the two tile parities, 16 registers each
+GW = 96                         # v[96:127]  dO^T operand, gw[ks] = v[96+4ks : +3]
+SETS = ((128, 144), (160, 176)) # (S^T / P / dS, dP^T) of the two tile parities, 16 registers each
 NRING = 6
-RING = 160                      # operand ring of K rows, V rows and dO^T reads (4 registers a slot)
+RING = 192                      # operand ring of K rows and V rows (4 registers a slot)
 NTR = 4
 TR = RING + 4 * NRING           # ring of transposed K operands (4 registers a slot)
-KADDR = TR + 4 * NTR            # 8: LDS byte address of this lane's K/V row chunk per ks (buffer 0)
-TRO = KADDR + 8                 # 8: LDS byte offsets of the transposed reads, index 4*half + db
-GWADDR = TRO + 8                # LDS byte address of this lane's dO^T slot 0
-OFFA = GWADDR + 1               # global byte offset of this lane's chunk in the row copies' next tile
-OFFB = OFFA + 1                 # ... in the transposed-read copy's next tile
-L2, DSUM = OFFB + 1, OFFB + 2
+KA = TR + 4 * NTR               # LDS byte address of this lane's row-operand chunk (buffer base)
+TRA = KA + 1                    # ... of this lane's 8 transposed bytes
+OFFA = KA + 2                   # global byte offset of this lane's chunk in the row copies' next tile
+OFFB = KA + 3                   # ... in the transposed-read copy's next tile
+L2, DSUM = KA + 4, KA + 5
 NREG = DSUM + 1
 
-OPERAND_REGS = set(range(DQ, DQ + 64)) | set(range(QW, QW + 32)) | set(range(KADDR, KADDR + 8)) | \
-    set(range(TRO, TRO + 8)) | {GWADDR, OFFA, OFFB, L2, DSUM}
+OPERAND_REGS = set(range(DQ, GW + 32)) | set(range(KA, NREG))
 LOOP_WRITTEN = list(range(DQ, DQ + 64)) + list(range(SETS[0][0], SETS[1][1] + 16))
 
 TILE = 32 * 128 * 2             # one 32-key tile of K or V (bytes, LDS and HBM)
 ROWS_K, KT, ROWS_V = 0, 2 * TILE, 4 * TILE   # LDS regions, two buffers each
-GW_STRIDE = 64 * 16             # bytes between a wave's dO^T slots of consecutive ks
 
 
 class Gen:
@@ -102,16 +103,14 @@ class Gen:
 
     def read_row(self, kind, ks, buf, slot):
         d = RING + 4 * slot
-        if kind == "g":
-            return self.e.lds_read(f"ds_read_b128 {rng(d, 4)}, v{GWADDR} offset:{ks * GW_STRIDE}", d, 4)
         region = ROWS_K if kind == "k" else ROWS_V
-        return self.e.lds_read(f"ds_read_b128 {rng(d, 4)}, v{KADDR + ks} offset:{region + buf * TILE}", d, 4)
+        return self.e.lds_read(f"ds_read_b128 {rng(d, 4)}, v{KA} offset:{region + buf * TILE + ks * 1024}", d, 4)
 
     def read_tr(self, ks2, db, buf, slot):
         d = TR + 4 * slot
-        off = KT + buf * TILE + ks2 * 16 * 16 * 16
-        self.e.lds_read(f"ds_read_b64_tr_b16 {rng(d, 2)}, v{TRO + db} offset:{off}", d, 2)
-        return self.e.lds_read(f"ds_read_b64_tr_b16 {rng(d + 2, 2)}, v{TRO + 4 + db} offset:{off}", d + 2, 2)
+        off = KT + buf * TILE + (ks2 * 4 + db) * 2 * 512
+        self.e.lds_read(f"ds_read_b64_tr_b16 {rng(d, 2)}, v{TRA} offset:{off}", d, 2)
+        return self.e.lds_read(f"ds_read_b64_tr_b16 {rng(d + 2, 2)}, v{TRA} offset:{off + 512}", d + 2, 2)
 
     # ------------------------------------------------------------ phases
     def phase_products(self, nxt, rbuf, ops, pre_ops=(), tr_first=None):
@@ -124,7 +123,7 @@ class Gen:
         s, dp = nxt
         reads = []
         for ks in range(8):
-            reads += [("k", ks), ("v", ks), ("g", ks)]
+            reads += [("k", ks), ("v", ks)]
         rid, nxt_read = {}, 0
 
         def issue_upto(limit):
@@ -141,17 +140,13 @@ class Gen:
         trid = {}
         for i in range(16):
             ks = i // 2
+            a = 2 * ks + (i % 2)
+            e.wait_lds(rid[a])
             if i % 2 == 0:
-                a = 3 * ks
-                e.wait_lds(rid[a])
                 e.mfma(self.mf, s, RING + 4 * (a % NRING), QW + 4 * ks, None if ks == 0 else s)
-                used = a + 1
             else:
-                a, g = 3 * ks + 1, 3 * ks + 2
-                e.wait_lds(rid[g])
-                e.mfma(self.mf, dp, RING + 4 * (a % NRING), RING + 4 * (g % NRING), None if ks == 0 else dp)
-                used = g + 1
-            issue_upto(used + NRING)
+                e.mfma(self.mf, dp, RING + 4 * (a % NRING), GW + 4 * ks, None if ks == 0 else dp)
+            issue_upto(a + 1 + NRING)
             if tr_first is not None and i >= 16 - NTR:
                 j = i - (16 - NTR)
                 trid[j] = self.read_tr(j // 4, j % 4, tr_first, j % NTR)
@@ -268,9 +263,8 @@ def main():
     vr = lambda r, n: f'"{{v[{r}:{r + n - 1}]}}"'
     outs = [f'"+{{v[{DQ + 16 * i}:{DQ + 16 * i + 15}]}}"(dq[{i}])' for i in range(4)]
     outs += [f'"+{{v{OFFA}}}"(offa)', f'"+{{v{OFFB}}}"(offb)', '[pairs] "+s"(pairs)', '[m0save] "=&s"(m0save)']
-    ins = [f'{vr(QW + 4 * i, 4)}(qw[{i}])' for i in range(8)]
-    ins += [f'{v(KADDR + i)}(ka[{i}])' for i in range(8)] + [f'{v(TRO + i)}(tr[{i}])' for i in range(8)]
-    ins += [f'{v(GWADDR)}(gwaddr)', f'{v(L2)}(l2)', f'{v(DSUM)}(dsum)']
+    ins = [f'{vr(QW + 4 * i, 4)}(qw[{i}])' for i in range(8)] + [f'{vr(GW + 4 * i, 4)}(gw[{i}])' for i in range(8)]
+    ins += [f'{v(KA)}(ka)', f'{v(TRA)}(tra)', f'{v(L2)}(l2)', f'{v(DSUM)}(dsum)']
     ins += ['[c] "s"(c)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)']
     text += ("\n// operands: fixed registers of the block bound to the kernel's variables\n"
              "#define ATTN_DQ_PIPE_OPERANDS \\\n    : " + ", \\\n      ".join(outs) +
