@@ -227,6 +227,17 @@ static void naive_and_backward()
                             ATTN_BF16_OUT_F32, P(W), bw, &empty) == ATTN_ERR_DTYPE);
     EXPECT(attnh::check_bwd(P(Q), P(K), P(V), P(O), P(G4 * 26), PF(L), dq, dk, dv, 1, 2, 8, 64, 0.1f, ATTN_BF16,
                             P(W), bw - 4, &empty) == ATTN_ERR_WORKSPACE);
+
+    // the gradient pipelines: d = 128 without a mask, while a head's rows
+    // (256 bytes each) and the distance from D to lse2 plus a head's lse2
+    // (4 (B H N + N) bytes) stay within 32-bit offsets
+    EXPECT(attnh::bwd_pipelined(128, false, 1, 32, 8192));
+    EXPECT(!attnh::bwd_pipelined(64, false, 1, 32, 8192));
+    EXPECT(!attnh::bwd_pipelined(128, true, 1, 32, 8192));
+    EXPECT(attnh::bwd_pipelined(128, false, 1, 1, 1 << 24) == false);           // 2^24 rows of 256 bytes
+    EXPECT(attnh::bwd_pipelined(128, false, 1, 1, (1 << 24) - 1));
+    EXPECT(!attnh::bwd_pipelined(128, false, 4096, 64, 4096));                  // 4 B H N = 2^32
+    EXPECT(attnh::bwd_pipelined(128, false, 2047, 64, 8192));                   // 4 (B H N + N) < 2^32
 }
 
 // Key chunks of the decode path: whole 32-key tiles, every key in exactly one
