@@ -120,3 +120,15 @@ def test_backward_long_sequence(attn):
     """B1 H8 N4096 d128 bf16 causal: every gradient against the oracle."""
     got, ref = run_bwd(attn, 1, 8, 4096, 128, "bf16", True, seed=72)
     check(got, ref, "bwd N4096")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [768, 1091])
+def test_backward_pipeline_ranges(attn, causal, N):
+    """d = 128 sizes where the gradient kernels' pipelined blocks run several
+    loop iterations and hand over to the compiler-scheduled loops at their
+    range ends: N a multiple of the 256-key workgroup (every key workgroup
+    pipelined) and a ragged N (the last key workgroup and the last query
+    tiles outside the blocks), with an odd number of heads."""
+    got, ref = run_bwd(attn, 1, 3, N, 128, "bf16", causal, seed=73)
+    check(got, ref, f"bwd pipeline ranges N{N} causal {causal}")
