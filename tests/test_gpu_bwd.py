@@ -123,12 +123,14 @@ def test_backward_long_sequence(attn):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [768, 1091])
+@pytest.mark.parametrize("N", [80, 768, 1091])
 def test_backward_pipeline_ranges(attn, causal, N):
     """d = 128 sizes where the gradient kernels' pipelined blocks run several
     loop iterations and hand over to the compiler-scheduled loops at their
     range ends: N a multiple of the 256-key workgroup (every key workgroup
-    pipelined) and a ragged N (the last key workgroup and the last query
-    tiles outside the blocks), with an odd number of heads."""
+    pipelined), a ragged N (the last key workgroup and the last query tiles
+    outside the blocks; at N = 1091 the last key workgroup's block has a
+    single pair of steps) and N = 80 (the dQ block over two 32-key tiles,
+    without loop iterations), with an odd number of heads."""
     got, ref = run_bwd(attn, 1, 3, N, 128, "bf16", causal, seed=73)
     check(got, ref, f"bwd pipeline ranges N{N} causal {causal}")
