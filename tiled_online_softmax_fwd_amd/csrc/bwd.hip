@@ -267,7 +267,8 @@ bwd_dkdv(BwdParams p)
         const int qb = N / BQ;
         if (p.pipe && k_wg + KW * NW <= N && qb > qa) {
             __shared__ __attribute__((aligned(16))) float s_ld[NW][2][64];   // lse2 and D per step, per wave
-            constexpr uint32_t TILE = 32 * CPR * 16, ROWQ = 0, ROWG = 2 * TILE;
+            static_assert(CPR * 16 == 256, "256-byte rows");
+            constexpr uint32_t TILE = 32 * 256, ROWQ = 0, ROWG = 2 * TILE;
             const int qs = qa * BQ;
             int pl = lane;
             asm volatile("" : "+v"(pl));
