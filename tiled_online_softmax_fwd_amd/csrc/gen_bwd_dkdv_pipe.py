@@ -99,10 +99,7 @@ class Gen:
     # ------------------------------------------------------------ scheduling
     def run(self, mfmas, ops):
         """mfmas: list of (reads, fn(regs)); ops: VOps spread over the matrix
-        slots (an op in slot i follows matrix op i, program order kept).  Reads
-        go through their pools in consumption order, each issued as soon as the
-        slot it reuses has been consumed."""
-        e = self.e
+        slots (an op in slot i follows matrix op i, program order kept)."""
         slots = spread(ops, len(mfmas)) if ops else []
         seq = []
         for i, (rd, fn) in enumerate(mfmas):
@@ -110,6 +107,13 @@ class Gen:
             for o, s in zip(ops, slots):
                 if s == i:
                     seq.append((o.reads, o.fn))
+        self.consume(seq)
+
+    def consume(self, seq):
+        """Emit the consumers of seq (each (reads, fn(regs))) in order.  Reads
+        go through their pools in consumption order, each issued as soon as the
+        slot it reuses has been consumed; a consumer waits for its newest read."""
+        e = self.e
         size, base = {"ring": NRING, "tr": NTR}, {"ring": RING, "tr": TR}
         stream = {"ring": [], "tr": []}
         cons = []
@@ -262,37 +266,8 @@ class Gen:
         overlap them with), then dV and dK."""
         cur = SETS[1]
         self.barrier()
-        self.run_plain([(o.reads, o.fn) for o in self.ds_ops(cur, 1, False, 99, 99)])
+        self.consume([(o.reads, o.fn) for o in self.ds_ops(cur, 1, False, 99, 99)])
         self.run(self.mf_grad("g", cur, 1) + self.mf_grad("q", DPS, 1), [])
-
-    def run_plain(self, items):
-        """Straight-line consumers (no matrix work to spread over)."""
-        e = self.e
-        size, base = NRING, RING
-        stream = []
-        cons = []
-        for rd, _ in items:
-            lst = []
-            for pool, emit in rd:
-                assert pool == "ring"
-                stream.append(emit)
-                lst.append(len(stream) - 1)
-            cons.append(lst)
-        rid, nxt, done = {}, 0, [False] * len(stream)
-
-        def issue():
-            nonlocal nxt
-            while nxt < len(stream) and (nxt < size or done[nxt - size]):
-                rid[nxt] = stream[nxt](base + 4 * (nxt % size))
-                nxt += 1
-        issue()
-        for (rd, fn), lst in zip(items, cons):
-            if lst:
-                e.wait_lds(max(rid[k] for k in lst))
-            fn([base + 4 * (k % size) for k in lst])
-            for k in lst:
-                done[k] = True
-            issue()
 
     def program(self):
         e = self.e
