@@ -24,6 +24,12 @@
 // dS are rounded to the input type for the MFMA, as P is in the forward.
 // Tiles read both row-wise and transposed (Q and dO here, K in bwd_dq) are
 // stored with swz_kt, under which neither read has LDS bank conflicts.
+// At d = 128 without a key-padding mask both gradient kernels first run their
+// full tiles (every pair visible, nothing past N) through generated
+// instruction-scheduled loops (bwd_dkdv_pipe_asm.h, bwd_dq_pipe_asm.h), which
+// keep the per-element arithmetic and accumulation order of the loops here and
+// copy their tiles in operand-ordered layouts; the loops here take the
+// diagonal and ragged tiles.
 #include <hip/hip_runtime.h>
 #include "bwd.h"
 #include "fwd_kernel.h"
