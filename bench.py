@@ -38,6 +38,8 @@ METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak; max|Δ| vs FP64 oracle"
 # default sources of a traffic record: the forward kernels, the generated
 # pipeline and the host planner (which picks tiles and the persistent grid)
 KERNEL_SOURCES = ["fwd_kernel.h", "fwd_pipe_asm.h", "attn_host.h"]
+# sources of the gradient kernels' traffic record
+BWD_SOURCES = ["bwd.hip", "bwd.h", "bwd_dq_pipe_asm.h", "bwd_dkdv_pipe_asm.h", "fwd_kernel.h", "attn_host.h"]
 
 
 def kernel_hash(sources=None):
@@ -424,6 +426,9 @@ def run_backward(args, torch, synth, A):
         for name, x, r in zip(("dq", "dk", "dv"), res["g"], (rq, rk, rv)):
             e = np.abs(x[:, :heads].to(torch.float64).cpu().numpy() - r)
             check[name] = {"max_abs": float(e.max()), "mean_abs": float(e.mean()), "max_ref": float(np.abs(r).max())}
+    # HBM bytes of the three kernels of one call, from the committed counter
+    # summary when it was taken on the current gradient sources
+    tr = traffic_record(f"backward_B{B}_H{H}_N{N}_d{d}_{args.dtype}_{'causal' if causal else 'full'}")
     line = {
         "metric": "attention backward TFLOP/s (5 products, halved for causal)", "value": fl / (wall / args.steps) / 1e12,
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -433,7 +438,8 @@ def run_backward(args, torch, synth, A):
                    "B": B, "H": H, "N": N, "d": d, "causal": causal},
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "bwd_pre + bwd_dkdv + bwd_dq",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
+                     "kernel": "bwd_pre + bwd_dkdv + bwd_dq",
                      "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
