@@ -40,6 +40,8 @@ METRIC = "attention fwd TFLOP/s and % bf16 MFMA peak; max|Δ| vs FP64 oracle"
 KERNEL_SOURCES = ["fwd_kernel.h", "fwd_pipe_asm.h", "attn_host.h"]
 # sources of the gradient kernels' traffic record
 BWD_SOURCES = ["bwd.hip", "bwd.h", "bwd_dq_pipe_asm.h", "bwd_dkdv_pipe_asm.h", "fwd_kernel.h", "attn_host.h"]
+# ... and of the block-sparse forward's
+SPARSE_SOURCES = ["fwd_kernel.h", "fwd_inst_sparse.hip", "attn_host.h"]
 
 
 def kernel_hash(sources=None):
@@ -526,6 +528,12 @@ def run_sparse(args, torch, synth, A):
         cpu = {"value": 4.0 * d * sample_pairs / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
                "kind": "oracle", "sample": f"all rows of {heads} of the {B * H} heads, {sample_pairs} attended pairs "
                                            f"(fp64 plain definition, {dt:.2f} s)"}
+    # HBM bytes per launch, from the committed counter summary when it was
+    # taken on the current sources (only the default window pattern has one)
+    tr = None
+    if args.pattern == "local_global" and not args.br and not args.bc:
+        tr = traffic_record(f"sparse_B{B}_H{H}_N{N}_d{d}_{args.dtype}_{'causal' if causal else 'full'}_block{blk}_"
+                            f"band{args.band}_global{args.n_global}")
     line = {
         "metric": "block-sparse attention fwd TFLOP/s over attended pairs", "value": fl / (wall / args.steps) / 1e12,
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -536,7 +544,8 @@ def run_sparse(args, torch, synth, A):
                    "attended_fraction": pairs / (B * H * N * N)},
         "check_vs_fp64_oracle": check,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "fwd_m32_h16 (block-sparse)",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
+                     "kernel": "fwd_m32_h16 (block-sparse)",
                      "kernel_ms_mean": float(kms.mean()), "kernel_ms_median": float(np.median(kms)), "kernel_ms_min": float(kms.min())},
         "cpu_baseline": cpu,
     }
