@@ -134,3 +134,23 @@ def test_backward_pipeline_ranges(attn, causal, N):
     without loop iterations), with an odd number of heads."""
     got, ref = run_bwd(attn, 1, 3, N, 128, "bf16", causal, seed=73)
     check(got, ref, f"bwd pipeline ranges N{N} causal {causal}")
+
+
+def test_backward_headline_shape_two_heads(attn):
+    """B1 H32 N8192 d128 bf16 causal, the shape and launch the backward
+    benchmark times (both gradient kernels' pipelined loops over their longest
+    ranges): the first and the last head's gradients against the oracle."""
+    import torch
+    B, H, N, d = 1, 32, 8192, 128
+    p = synth.make_qkv(B, H, N, d, "bf16", 74)
+    g = synth.make_qkv(B, H, N, d, "bf16", 74, variant=1)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    q, k, v = synth.upload(p)
+    dout = synth.to_torch(g.q, "bf16")
+    o, lse = attn.fwd(q, k, v, scale=scale, causal=True)
+    dq, dk, dv = attn.bwd(q, k, v, o, dout, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    hs = [0, H - 1]
+    ref = oracle.attn_bwd(p.q64[:, hs], p.k64[:, hs], p.v64[:, hs], g.q64[:, hs], scale, True)
+    got = tuple(gu.host(x)[:, hs] for x in (dq, dk, dv))
+    check(got, ref, "bwd B1 H32 N8192 heads 0, 31")
