@@ -196,3 +196,16 @@ def test_degenerate_sizes(attn):
         o, l = attn.fwd_sparse(z, z, z, bm, block=64)
         torch.cuda.synchronize()
         assert o.shape == z.shape
+
+
+def test_benchmark_window_at_full_size(attn):
+    """The block-sparse benchmark's workload: B1 H32 N8192 d128 bf16 causal,
+    blocks of 64, a window of +-4 blocks plus one global block, default tiles
+    (the launch the benchmark times); every row of every head against the
+    oracle."""
+    import math
+    p = synth.make_qkv(1, 32, 8192, 128, "bf16", 5)
+    bm = synth.block_mask(1, 32, 8192, 64, 5, "local_global", 0.5, 4, 1)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    say("sparse benchmark window B1 H32 N8192 d128 causal")
+    check(attn, p, bm, 64, scale, True, what="sparse window +-4 + global, B1 H32 N8192")
