@@ -17,7 +17,9 @@ struct BwdParams {
     float* dv;
     const uint8_t* mask;    // [B][N] or nullptr
     float* dsum;            // [B][H][N] workspace: sum_c dO O
-    float* lse2;            // [B][H][N] workspace: lse * log2(e), +inf for empty rows
+    float* lse2;            // [B][H][N] workspace: lse * log2(e), +inf for empty rows; it follows
+                            // dsum in the same workspace (the dK/dV pipeline addresses a head's
+                            // lse2 from its dsum with 32-bit offsets, which the host gate sizes)
     int B, H, N;
     float scale;            // natural-log factor of q.k
     float c;                // scale * log2(e)
