@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) bwd_pre(BwdParams p)
 #pragma unroll
     for (int w = LPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w);
     if (row < rows && part == 0) {
-        p.dsum[row] = acc;
+        p.dsum[row] = -acc;     // minus D: the dP products of dK/dV accumulate onto it
         const float l = p.lse[row];
         p.lse2[row] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
     }
@@ -421,10 +421,18 @@ bwd_dkdv(BwdParams p)
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) dv[kb][db] = TR::mma32(pa[kb][t], gt, dv[kb][db]);
                 }
-            // dP = dO V^T, then dS = P (dP - D) in place
+            // dP - D = dO V^T - D: the products accumulate onto -D of the
+            // lane's rows (the workspace holds -D), read as four 16-byte
+            // vectors straight into the accumulator; then dS = P (dP - D)
             f32x16 dp[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) dp[kb] = (f32x16){};
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 nd4 = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dp[kb][4 * g4 + i] = nd4[i];
+            }
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
                 const u32x4 ga = sg[buf][(32 * h + col) * CPR + swz_kt<CPR>(32 * h + col, ks * 2 + hh)];
@@ -432,21 +440,10 @@ bwd_dkdv(BwdParams p)
                 for (int kb = 0; kb < KB; ++kb)
                     dp[kb] = TR::mma32(__builtin_bit_cast(v8, ga), __builtin_bit_cast(v8, s_vw[wave][kb][ks][lane]), dp[kb]);
             }
-            // dS = P (dP - D), D of the same rows read as four 16-byte vectors
-            // (each where its rows are used at d = 128, all first at d = 64)
-            f32x4 dse[LATE ? 1 : 4];
-            if constexpr (!LATE) {
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) dse[g4] = *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh];
-            }
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 dsv = LATE ? *(const f32x4*)&s_d[buf][32 * h + 8 * g4 + 4 * hh] : dse[LATE ? 0 : g4];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dp[kb][4 * g4 + i] = s[kb][4 * g4 + i] * (dp[kb][4 * g4 + i] - dsv[i]);
-            }
+                for (int j = 0; j < 16; ++j) dp[kb][j] = s[kb][j] * dp[kb][j];
             v8 da[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -526,7 +523,7 @@ bwd_dq(BwdParams p)
     const int qi = wave_q0 + col;                     // this lane's query
     const int qrow = min(qi, N - 1);
     const float l2 = qi < N ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
-    const float dsum = p.dsum[(size_t)bh * N + qrow];
+    const float ndsum = p.dsum[(size_t)bh * N + qrow];   // minus D
     const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * N : nullptr;
     // MASKED: padw[kb][g4] holds the flags of keys k0 + 32*kb + 8*g4 + 4*hh +
     // 0..3 of the current tile, padn those of the next; one 32-bit load when
@@ -688,7 +685,7 @@ bwd_dq(BwdParams p)
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s[kb][j] = s[kb][j] * (dp[kb][j] - dsum);
+                for (int j = 0; j < 16; ++j) s[kb][j] = s[kb][j] * (dp[kb][j] + ndsum);
             };
             // dQ^T += K^T dS^T over the 16 keys of chunk ks2
             auto dq_chunk = [&](int ks2) __attribute__((always_inline)) {

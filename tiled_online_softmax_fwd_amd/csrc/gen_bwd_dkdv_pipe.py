@@ -5,13 +5,15 @@ workgroup).
 
 The block covers the 32-query steps whose rows see every key of the
 workgroup.  Per step t the wave computes S = Q K^T and dP = dO V^T (8
-products each), P = exp2(S c - lse2), dS = P (dP - D), both rounded to the
-input type, then dV += P^T dO and dK += dS^T Q (8 products each).  It is a
-two-stage software pipeline over steps; iteration t issues, in this order,
-    S(t+1)   beside dS(t) and the rounding of P(t) and dS(t),
-    dV(t),
-    dK(t)    beside the exponentials of step t+1,
-    dP(t+1).
+products each; dP accumulates onto -D, which the workspace holds), P =
+exp2(S c - lse2), dS = P (dP - D), both rounded to the input type, then
+dV += P^T dO and dK += dS^T Q (8 products each).  It is a two-stage software
+pipeline over steps; iteration t issues, in this order,
+    S(t+1)   beside dS(t) and its rounding,
+    dK(t)    beside the rounding of P(t),
+    dV(t)    beside the exponentials of step t+1 (-D of step t+1 is read
+             into the dP accumulator after the last dK product),
+    dP(t+1)  beside the rest of those exponentials.
 Per element, every operation and its order are those of the compiler-scheduled
 loop in bwd.hip, so the results are bitwise equal; only the interleaving of
 independent instructions differs.
@@ -84,7 +86,8 @@ class Gen:
 
     def rd_ld(self, kind, g4, buf):
         e = self.e
-        off = buf * LDSLOT + g4 * 32 + (128 if kind == "d" else 0)
+        assert kind == "l"
+        off = buf * LDSLOT + g4 * 32
         return ("ring", lambda d: e.lds_read(f"ds_read_b128 {rng(d, 4)}, v{LDA} offset:{off}", d, 4))
 
     def rd_tr(self, kind, tt, db, buf):
@@ -172,30 +175,30 @@ class Gen:
         return [VOp(lambda _, r=r: e.valu(f"v_add_u32 v{r}, 0x{TILE:x}, v{r}", (r,), (r,)), 4) for r in regs]
 
     # ------------------------------------------------------------ work of one step
-    def ds_ops(self, cur, p, copy_next, hi_p, hi_ds):
-        """dS = P (dP - D) in place in DPS (D of rows 8 g4 + 4 hh + i), then P
-        and dS rounded to the input type in place (chunk tt packed into the
-        first 4 registers of base + 8 tt).  copy_next: once the last D vector
-        is read, the slot takes lse2 / D of step t+2."""
+    def ds_ops(self, cur, hi_ds, hi_p):
+        """dS = P (dP - D) in place in DPS (the dP accumulator started at -D),
+        then dS and P rounded to the input type in place (chunk tt packed into
+        the first 4 registers of base + 8 tt)."""
         e, ops = self.e, []
-        for g4 in range(4):
-            def fn(regs, g4=g4):
-                for i in range(4):
-                    r = DPS + 4 * g4 + i
-                    e.valu(f"v_sub_f32 v{r}, v{r}, v{regs[0] + i}", (r, regs[0] + i), (r,))
-                if g4 == 3 and copy_next:
-                    self.dma_ld(p)
-            ops.append(VOp(fn, 16 + (8 if g4 == 3 and copy_next else 0), hi=hi_p, reads=[self.rd_ld("d", g4, p)]))
         for j in range(16):
             a, b = cur + j, DPS + j
-            ops.append(VOp(lambda _, a=a, b=b: e.valu(f"v_mul_f32 v{b}, v{a}, v{b}", (a, b), (b,)), 4, hi=hi_p))
-        for base, hi in ((cur, hi_p), (DPS, hi_ds)):
+            ops.append(VOp(lambda _, a=a, b=b: e.valu(f"v_mul_f32 v{b}, v{a}, v{b}", (a, b), (b,)), 4, hi=hi_ds))
+        for base, hi in ((DPS, hi_ds), (cur, hi_p)):
             for tt in range(2):
                 for i in range(0, 8, 2):
                     d, a, b = base + 8 * tt + i // 2, base + 8 * tt + i, base + 8 * tt + i + 1
                     ops.append(VOp(lambda _, d=d, a=a, b=b: e.valu(f"{self.cvt} v{d}, v{a}, v{b}", (a, b), (d,)), 4,
                                    hi=hi))
         return ops
+
+    def read_nd(self, buf):
+        """-D of a step's rows (8 g4 + 4 hh + i) from the wave's slot buf
+        straight into the dP accumulator; returns the last read's id."""
+        e, rid = self.e, None
+        for g4 in range(4):
+            d = DPS + 4 * g4
+            rid = e.lds_read(f"ds_read_b128 {rng(d, 4)}, v{LDA} offset:{buf * LDSLOT + 128 + g4 * 32}", d, 4)
+        return rid
 
     def exp_ops(self, s, buf, lo):
         """P = exp2(S c - lse2) in place (lse2 of rows 8 g4 + 4 hh + i)."""
@@ -218,19 +221,31 @@ class Gen:
                 for ks in range(8)]
 
     def mf_dp(self, buf):
+        """dP accumulated onto the -D already read into DPS (self.nd_rid)."""
         e = self.e
+
+        def first(regs):
+            e.wait_lds(self.nd_rid)
+            e.mfma(self.mf, DPS, regs[0], regs[1], DPS)
         return [([self.rd_row("g", ks, buf), self.rd_row("v", ks, None)],
-                 lambda regs, ks=ks: e.mfma(self.mf, DPS, regs[0], regs[1], None if ks == 0 else DPS))
+                 first if ks == 0 else (lambda regs: e.mfma(self.mf, DPS, regs[0], regs[1], DPS)))
                 for ks in range(8)]
 
-    def mf_grad(self, kind, src, buf):
+    def mf_grad(self, kind, src, buf, after_last=None):
         """dV += P^T dO (kind 'g') or dK += dS^T Q (kind 'q'), chunks tt = 0, 1
-        of the step's 32 rows for each 32-column block db."""
+        of the step's 32 rows for each 32-column block db; after_last() is
+        emitted right after the last product."""
         e = self.e
         acc = DV if kind == "g" else DK
+        items = [(tt, db) for tt in range(2) for db in range(4)]
+
+        def fn(regs, tt, db, last):
+            e.mfma(self.mf, acc + 16 * db, src + 8 * tt, regs[0], acc + 16 * db)
+            if last and after_last is not None:
+                after_last()
         return [([self.rd_tr(kind, tt, db, buf)],
-                 lambda regs, tt=tt, db=db: e.mfma(self.mf, acc + 16 * db, src + 8 * tt, regs[0], acc + 16 * db))
-                for tt in range(2) for db in range(4)]
+                 lambda regs, tt=tt, db=db, last=(n == len(items) - 1): fn(regs, tt, db, last))
+                for n, (tt, db) in enumerate(items)]
 
     # ------------------------------------------------------------ program
     def iteration(self, p, last):
@@ -240,11 +255,17 @@ class Gen:
         if not last:
             self.dma16(ROWQ, p, "%[qbase]", OFFR)
             self.dma16(ROWG, p, "%[gbase]", OFFR)
+            # the slot held lse2 and -D of step t, both read in iteration t-1
+            self.dma_ld(p)
         self.dma16(TRQ, 1 - p, "%[qbase]", OFFT)
         self.dma16(TRG, 1 - p, "%[gbase]", OFFT)
-        mf = self.mf_s(nxt, 1 - p) + self.mf_grad("g", cur, p) + self.mf_grad("q", DPS, p) + self.mf_dp(1 - p)
+
+        def nd():
+            self.nd_rid = self.read_nd(1 - p)
+        mf = (self.mf_s(nxt, 1 - p) + self.mf_grad("q", DPS, p, after_last=nd) + self.mf_grad("g", cur, p) +
+              self.mf_dp(1 - p))
         ops = self.offset_ops(((OFFR,) if not last else ()) + (OFFT,))
-        ops += self.ds_ops(cur, p, not last, 7, 15)
+        ops += self.ds_ops(cur, 7, 15)
         ops += self.exp_ops(nxt, 1 - p, 9)
         self.run(mf, ops)
 
@@ -258,16 +279,17 @@ class Gen:
         self.dma16(TRQ, 0, "%[qbase]", OFFT)
         self.dma16(TRG, 0, "%[gbase]", OFFT)
         self.dma_ld(1)
+        self.nd_rid = self.read_nd(0)
         ops = self.offset_ops((OFFR, OFFT)) + self.exp_ops(SETS[0], 0, 9)
         self.run(self.mf_s(SETS[0], 0) + self.mf_dp(0), ops)
 
     def epilogue(self):
         """Last step (t = n-1, odd): dS and the rounding (nothing left to
-        overlap them with), then dV and dK."""
+        overlap them with), then dK and dV."""
         cur = SETS[1]
         self.barrier()
-        self.consume([(o.reads, o.fn) for o in self.ds_ops(cur, 1, False, 99, 99)])
-        self.run(self.mf_grad("g", cur, 1) + self.mf_grad("q", DPS, 1), [])
+        self.consume([(o.reads, o.fn) for o in self.ds_ops(cur, 99, 99)])
+        self.run(self.mf_grad("q", DPS, 1) + self.mf_grad("g", cur, 1), [])
 
     def program(self):
         e = self.e

@@ -45,7 +45,7 @@ KA = TR + 4 * NTR               # LDS byte address of this lane's row-operand ch
 TRA = KA + 1                    # ... of this lane's 8 transposed bytes
 OFFA = KA + 2                   # global byte offset of this lane's chunk in the row copies' next tile
 OFFB = KA + 3                   # ... in the transposed-read copy's next tile
-L2, DSUM = KA + 4, KA + 5
+L2, DSUM = KA + 4, KA + 5       # lse2 and minus D of this lane's query
 NREG = DSUM + 1
 
 OPERAND_REGS = set(range(DQ, GW + 32)) | set(range(KA, NREG))
@@ -76,7 +76,7 @@ class Gen:
             ops.append(Op(lambda r=r: e.valu(f"v_exp_f32 v{r}, v{r}", (r,), (r,), trans=True), 8))
         for j in range(16):
             r = dp + j
-            ops.append(Op(lambda r=r: e.valu(f"v_sub_f32 v{r}, v{r}, v{DSUM}", (r, DSUM), (r,)), 4))
+            ops.append(Op(lambda r=r: e.valu(f"v_add_f32 v{r}, v{r}, v{DSUM}", (r, DSUM), (r,)), 4))
         for j in range(16):
             a, b = s + j, dp + j
             ops.append(Op(lambda a=a, b=b: e.valu(f"v_mul_f32 v{a}, v{a}, v{b}", (a, b), (a,)), 4))
@@ -264,7 +264,7 @@ def main():
     outs = [f'"+{{v[{DQ + 16 * i}:{DQ + 16 * i + 15}]}}"(dq[{i}])' for i in range(4)]
     outs += [f'"+{{v{OFFA}}}"(offa)', f'"+{{v{OFFB}}}"(offb)', '[pairs] "+s"(pairs)', '[m0save] "=&s"(m0save)']
     ins = [f'{vr(QW + 4 * i, 4)}(qw[{i}])' for i in range(8)] + [f'{vr(GW + 4 * i, 4)}(gw[{i}])' for i in range(8)]
-    ins += [f'{v(KA)}(ka)', f'{v(TRA)}(tra)', f'{v(L2)}(l2)', f'{v(DSUM)}(dsum)']
+    ins += [f'{v(KA)}(ka)', f'{v(TRA)}(tra)', f'{v(L2)}(l2)', f'{v(DSUM)}(ndsum)']
     ins += ['[c] "s"(c)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)']
     text += ("\n// operands: fixed registers of the block bound to the kernel's variables\n"
              "#define ATTN_DQ_PIPE_OPERANDS \\\n    : " + ", \\\n      ".join(outs) +
