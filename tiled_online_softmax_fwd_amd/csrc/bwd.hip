@@ -168,10 +168,13 @@ __device__ __forceinline__ typename H16<T>::v8 pack8(const f32x16& x, int ks2)
 // wave reads from LDS (row-major for S and dP, transposed for dK and dV) serve
 // all KB blocks, so LDS bytes per matrix product fall as KB grows (at d = 128,
 // KB = 2 needs four waves, one per SIMD, with 256 accumulator registers).
+// With KB = 1 the registers are capped for two waves per SIMD: two per
+// workgroup at d = 128, and at d = 64 (four-wave workgroups) two workgroups
+// per compute unit, whose tiles then hide each other's latencies.
 // MASKED (calls with a key-padding mask): a wave whose keys are all padded
 // takes part in the copies and barriers only (its dK and dV stay zero).
 template <typename T, int D, int NW, int KB, bool MASKED = false>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KB == 1 ? NW / 4 : 1, KB == 1 ? NW / 4 : 1)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KB == 1 ? 2 : 1, KB == 1 ? 2 : 1)))
 bwd_dkdv(BwdParams p)
 {
     using TR = H16<T>;
@@ -484,9 +487,10 @@ bwd_dkdv(BwdParams p)
 // MASKED (calls with a key-padding mask): each lane's padding flags of the next
 // key tile are loaded one tile ahead (a 32-bit word holds the flags of four
 // consecutive keys); a tile without a padded key takes the unmasked path and
-// a tile whose keys are all padded is skipped.
+// a tile whose keys are all padded is skipped.  Registers are capped for two
+// waves per SIMD (at d = 64, two four-wave workgroups per compute unit).
 template <typename T, int D, int NW, bool MASKED = false>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_dq(BwdParams p)
 {
     using TR = H16<T>;
@@ -727,7 +731,8 @@ template <typename T, int D>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st)
 {
     // eight waves (two per SIMD) at d = 128; at d = 64 a 32-row tile has too
-    // few 16-byte chunks for eight waves' copy instructions, so four
+    // few 16-byte chunks for eight waves' copy instructions, so four, and two
+    // workgroups share a compute unit
     constexpr int NW = D == 128 ? 8 : 4;
     const size_t rows = (size_t)p.B * p.H * p.N;
     constexpr size_t RPB = 256 / (D / 8);            // rows per block of bwd_pre
