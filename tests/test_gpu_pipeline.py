@@ -30,12 +30,13 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def both(A, p, scale, causal, out_fp32):
+def both(A, p, scale, causal, out_fp32, ref_slack=0):
     import torch
     q, k, v = gu.upload(p)
     outs = []
     for generic in (False, True):
-        o, l = A.fwd(q, k, v, scale=scale, causal=causal, out_fp32=out_fp32, generic_loop=generic)
+        o, l = A.fwd(q, k, v, scale=scale, causal=causal, out_fp32=out_fp32, generic_loop=generic,
+                     ref_slack=ref_slack)
         outs.append((o, l))
     torch.cuda.synchronize()
     return outs
@@ -98,6 +99,25 @@ def test_pipelined_peaked_rows_bitwise(attn):
         (o1, l1), (o2, l2) = both(attn, p, scale, causal, True)
         assert torch.equal(o1, o2)
         assert torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("slack", [1, 8])
+@pytest.mark.parametrize("B,H,N,causal", [(1, 2, 200, True), (2, 2, 512, False), (1, 4, 1000, True),
+                                          (1, 32, 4096, True)])
+def test_pipelined_lagging_reference_bitwise(attn, slack, B, H, N, causal):
+    """With ref_slack the pipeline compares c (mt - m) against the slack
+    instead of 0; both loops then move the reference on the same tiles."""
+    import torch
+    p = synth.make_qkv(B, H, N, 128, "bf16", 76, variant=N + slack)
+    scale = float(np.float32(128 ** -0.5))
+    say("pipeline vs tile loop, ref_slack", slack, B, H, N, "causal", causal)
+    (o1, l1), (o2, l2) = both(attn, p, scale, causal, False, ref_slack=slack)
+    assert torch.equal(o1, o2), f"O differs: max {float((o1.double() - o2.double()).abs().max()):.3e}"
+    assert torch.equal(l1, l2), "lse differs"
+    if N <= 1000:
+        ro, rl = oracle.attn(p.q64, p.k64, p.v64, scale, causal)
+        gu.assert_close(gu.host(o1).astype(np.float64), ro, gu.TOL_H16, f"ref_slack {slack} O")
+        gu.assert_lse(gu.host(l1), rl, gu.TOL_LSE_H16, f"ref_slack {slack} lse")
 
 
 # Shapes whose work splits evenly over 256 compute units run on the persistent

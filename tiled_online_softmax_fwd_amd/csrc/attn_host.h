@@ -214,9 +214,10 @@ inline int64_t fwd_grid(const FwdPlan& p)
     return p.persist > 0 ? (int64_t)p.persist : (int64_t)p.B * p.H * p.n_qt;
 }
 
-// The 16-bit d = 128 kernel with 256 x 64 tiles, no mask, ascending keys and
-// the exact reference runs its full unmasked key tiles through the software
-// pipeline (unless generic_loop asks for the compiler-scheduled loop).
+// The 16-bit d = 128 kernel with 256 x 64 tiles, no mask and ascending keys
+// runs its full unmasked key tiles through the software pipeline, with the
+// exact or the lagging reference (unless generic_loop asks for the
+// compiler-scheduled loop).
 inline bool fwd_pipelined(const FwdPlan& p)
 {
 #ifdef ATTN_LDS_POISON
@@ -227,7 +228,7 @@ inline bool fwd_pipelined(const FwdPlan& p)
     return false;
 #else
     return p.dtype != ATTN_F32 && !p.sparse && !p.mask && p.d == 128 && p.br == 256 && p.bc == 64 &&
-           !p.generic && p.order == 0 && p.slack == 0;
+           !p.generic && p.order == 0;
 #endif
 }
 

@@ -849,11 +849,11 @@ fwd_m32_h16(FwdParams p)
         }
     };
 
-    // Steady state (16-bit, d = 128, 256 x 64, ascending order, exact
-    // reference): the key tiles that are full and need no mask for any row of
-    // the workgroup run through the software pipeline of fwd_pipe_asm.h (the
-    // score products of tile t+1 beside the softmax of tile t, then P.V of
-    // tile t beside the maximum of tile t+1).  It does this body's operations
+    // Steady state (16-bit, d = 128, 256 x 64, ascending order, the exact or
+    // the lagging reference): the key tiles that are full and need no mask
+    // for any row of the workgroup run through the software pipeline of
+    // fwd_pipe_asm.h (the score products of tile t+1 beside the softmax of
+    // tile t, then P.V of tile t beside the maximum of tile t+1).  It does this body's operations
     // in this body's order per row.  It consumes the K/V copies issued above
     // and leaves the next tile's copies in flight in the buffers the loop
     // below expects (an even count of tiles), with m, l and o updated.
@@ -861,7 +861,7 @@ fwd_m32_h16(FwdParams p)
     if constexpr (!SPARSE && !MASKED && D == 128 && BR == 256 && BC == 64) {
         int n_st = p.causal ? (q0 + 1) / BC : N / BC;
         n_st = min(min(n_st, N / BC), kt_end) & ~1;
-        if (p.pipe && order == 0 && p.slack == 0.f && n_st >= 2) {
+        if (p.pipe && order == 0 && n_st >= 2) {
             const uint32_t skb = lds_addr(sk[0]), svb = lds_addr(sv[0]);
             const uint32_t* ka = kaddr;
             const uint32_t* va = vaddr;
@@ -878,6 +878,7 @@ fwd_m32_h16(FwdParams p)
             const uint32_t has_next = __builtin_amdgcn_readfirstlane(next_full ? 1u : 0u);
             uint64_t moved;
             uint32_t m0save;
+            const float slack = p.slack;
             static_assert(KPlan::NI == 2 && VPlan::NI == 2, "pipeline copy plan");
             if constexpr (std::is_same<T, __bf16>::value)
                 asm volatile(ATTN_PIPE_ASM_BF16 ATTN_PIPE_OPERANDS);

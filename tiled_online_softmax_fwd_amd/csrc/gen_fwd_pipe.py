@@ -301,9 +301,10 @@ class Gen:
         return ops
 
     def refstep_ops(self):
-        """Row maximum across the two wave halves, then the exact-maximum
-        reference step: moved = c (mt - m) > 0; m' = moved ? mt : m;
-        alpha = moved ? exp2(c (m - m')) : 1; -m' c for the exponents."""
+        """Row maximum across the two wave halves, then the reference step:
+        moved = c (mt - m) > slack (0: the exact running maximum); m' = moved
+        ? mt : m; alpha = moved ? exp2(c (m - m')) : 1; -m' c for the
+        exponents."""
         e = self.e
         ops = [
             Op(lambda: e.valu(f"v_mov_b32 v{T0}, v{MT}", (MT,), (T0,)), 4),
@@ -311,7 +312,7 @@ class Gen:
             Op(lambda: e.valu(f"v_max_f32 v{MT}, v{MT}, v{T0}", (MT, T0), (MT,)), 4),
             Op(lambda: e.valu(f"v_sub_f32 v{T0}, v{MT}, v{M}", (MT, M), (T0,)), 4),
             Op(lambda: e.valu(f"v_mul_f32 v{T0}, %[c], v{T0}", (T0,), (T0,)), 4),
-            Op(lambda: e.valu(f"v_cmp_lt_f32 vcc, 0, v{T0}", (T0,), (), writes_vcc=True), 4),
+            Op(lambda: e.valu(f"v_cmp_lt_f32 vcc, %[slack], v{T0}", (T0,), (), writes_vcc=True), 4),
             Op(lambda: e.valu(f"v_cndmask_b32 v{T1}, v{M}, v{MT}, vcc", (M, MT), (T1,), reads_vcc=True), 4),
             Op(lambda: e.salu_reads_vcc("s_mov_b64 %[moved], vcc"), 1),
             Op(lambda: e.valu(f"v_sub_f32 v{ALPHA}, v{M}, v{T1}", (M, T1), (ALPHA,)), 4),
@@ -564,7 +565,7 @@ def main():
              '[pairs] "+s"(pairs)', '[moved] "=&s"(moved)', '[m0save] "=&s"(m0save)']
     ins = [f'{vr(Q + 4 * i, 4)}(qf[{i}])' for i in range(8)]
     ins += [f'{v(KADDR + i)}(ka[{i}])' for i in range(8)] + [f'{v(VADDR + i)}(va[{i}])' for i in range(4)]
-    ins += ['[c] "s"(c)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)', '[vdst] "s"(vdst)',
+    ins += ['[c] "s"(c)', '[slack] "s"(slack)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)', '[vdst] "s"(vdst)',
             '[has_next] "s"(has_next)']
     text += ("\n// operands: fixed registers of the block bound to the kernel's variables\n"
              "#define ATTN_PIPE_OPERANDS \\\n    : " + ", \\\n      ".join(outs) +
