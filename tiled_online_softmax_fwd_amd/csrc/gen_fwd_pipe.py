@@ -565,8 +565,8 @@ def main():
              '[pairs] "+s"(pairs)', '[moved] "=&s"(moved)', '[m0save] "=&s"(m0save)']
     ins = [f'{vr(Q + 4 * i, 4)}(qf[{i}])' for i in range(8)]
     ins += [f'{v(KADDR + i)}(ka[{i}])' for i in range(8)] + [f'{v(VADDR + i)}(va[{i}])' for i in range(4)]
-    ins += ['[c] "s"(c)', '[slack] "s"(slack)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)', '[vdst] "s"(vdst)',
-            '[has_next] "s"(has_next)']
+    ins += ['[c] "s"(c)', '[slack] "s"(slack)', '[kbase] "s"(kbase)', '[vbase] "s"(vbase)', '[kdst] "s"(kdst)',
+            '[vdst] "s"(vdst)', '[has_next] "s"(has_next)']
     text += ("\n// operands: fixed registers of the block bound to the kernel's variables\n"
              "#define ATTN_PIPE_OPERANDS \\\n    : " + ", \\\n      ".join(outs) +
              " \\\n    : " + ", \\\n      ".join(ins) + " \\\n    : ATTN_PIPE_CLOBBERS\n")
