@@ -528,7 +528,6 @@ bwd_dq(BwdParams p)
     const int qrow = min(qi, N - 1);
     const float l2 = qi < N ? p.lse2[(size_t)bh * N + qrow] : INFINITY;
     const float ndsum = p.dsum[(size_t)bh * N + qrow];   // minus D
-    const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * N : nullptr;
     // MASKED: padw[kb][g4] holds the flags of keys k0 + 32*kb + 8*g4 + 4*hh +
     // 0..3 of the current tile, padn those of the next; one 32-bit load when
     // the mask row is 4-byte aligned and the keys lie inside the row, else four
@@ -656,7 +655,7 @@ bwd_dq(BwdParams p)
         // lse2 = +inf); the empty asm keeps each one out of a per-element
         // branch, and the visibility test runs only on tiles that are not
         // wholly visible.
-        const bool all = !mrow && !pad_any && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
+        const bool all = !pad_any && k0 + BC <= N && wave_q0 + 31 < N && (!p.causal || k0 + BC - 1 <= wave_q0);
         {
             f32x16 s[NKB], dp[NKB];
             auto products = [&](int kb) __attribute__((always_inline)) {
@@ -684,7 +683,6 @@ bwd_dq(BwdParams p)
                         bool vis = key < N && qi < N;
                         if (p.causal) vis = vis && key <= qi;
                         if constexpr (MASKED) vis = vis && ((padw[kb][j >> 2] >> (8 * (j & 3))) & 0xffu) == 0;
-                        if (mrow) vis = vis && mrow[min(key, N - 1)] == 0;
                         s[kb][j] = vis ? s[kb][j] : 0.f;
                     }
                 }

@@ -64,7 +64,6 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
     if (p.causal) k_hi = min(k_hi, Nk - Nq + min(blockIdx.y * 16 + 15, Nq - 1) + 1);
     const int ntile = k_hi > k_lo ? (k_hi - k_lo + BC - 1) / BC : 0;
     const int last = p.causal ? Nk - Nq + qi : Nk - 1;   // last key this row sees
-    const uint8_t* mrow = (!MASKED && p.mask) ? p.mask + (size_t)b * Nk : nullptr;
     // MASKED: padw[kb] holds the flags of keys k0 + 16*kb + 4*g + 0..3 of the
     // current tile, padn those of the next one; one 32-bit load when the mask
     // row is 4-byte aligned and the keys lie inside the row, else four byte
@@ -159,7 +158,6 @@ __global__ void __launch_bounds__(64) dec_split(DecParams p)
                 const int key = k0 + kb * 16 + 4 * g + i;
                 bool vis = key < k_hi && key <= last;
                 if constexpr (MASKED) vis = vis && (!pad_any || ((padw[kb] >> (8 * i)) & 0xffu) == 0);
-                if (mrow) vis = vis && mrow[min(key, Nk - 1)] == 0;
                 if (!vis) s[kb][i] = -INFINITY;
             }
         }
